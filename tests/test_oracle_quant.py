@@ -1,0 +1,99 @@
+"""Pins for the oracle's per-group quantizer, nibble packing and dequant."""
+import numpy as np
+import pytest
+
+import oracle
+
+Q = oracle.quant
+
+
+def test_hand_built_group_codes():
+    # absmax 7 -> s32 = 1 exactly (fp16-exact); t = y exactly
+    y = np.array([[7.0, 2.5, -2.5, 0.5, -0.5, 1.5, -1.49, 0.0]])
+    codes, scales, s_used = Q.quantize_groups(y, 8, "f16")
+    assert scales.dtype == np.float16 and float(scales[0, 0]) == 1.0
+    # ties round away from zero
+    assert codes.tolist() == [[7, 3, -3, 1, -1, 2, -1, 0]]
+
+
+def test_negative_absmax_gets_minus_seven():
+    y = np.array([[-3.5, 1.0, 0.25, -0.75]])
+    codes, scales, _ = Q.quantize_groups(y, 4, "f32")
+    assert float(scales[0, 0]) == np.float32(np.float32(3.5) / np.float32(7))
+    assert codes[0, 0] == -7 and codes[0, 1] == 2
+
+
+def test_fp16_scale_rounding():
+    y = np.array([[0.7, -0.1, 0.3, 0.0]])
+    codes, scales, s_used = Q.quantize_groups(y, 4, "f16")
+    s32 = np.float32(np.float32(0.7) / np.float32(7))
+    assert scales[0, 0] == np.float16(s32)
+    assert float(s_used[0, 0]) == float(np.float16(s32))
+    # codes are taken against the stored (fp16) scale
+    t = np.float32(np.float32(0.3) / s_used[0, 0])
+    assert codes[0, 2] == int(np.floor(t + 0.5))
+
+
+def test_zero_group_and_mixed_groups():
+    y = np.zeros((2, 8))
+    y[1, 4:] = [1.0, -2.0, 3.5, 0.0]
+    codes, scales, _ = Q.quantize_groups(y, 4, "f16")
+    assert np.all(codes[0] == 0) and np.all(scales[0] == 0)
+    assert np.all(codes[1, :4] == 0) and scales[1, 0] == 0
+    assert codes[1, 4:].tolist() == [2, -4, 7, 0]
+
+
+def test_absmax_element_is_seven_random():
+    rng = np.random.default_rng(1)
+    y = rng.standard_normal((64, 2048)) * rng.uniform(0.01, 100, size=(64, 1))
+    for mode in ("f16", "f32"):
+        codes, _, _ = Q.quantize_groups(y, 128, mode)
+        g = np.abs(y.astype(np.float32)).reshape(64, 16, 128)
+        c = np.abs(codes.reshape(64, 16, 128))
+        idx = g.argmax(-1)
+        assert np.all(np.take_along_axis(c, idx[..., None], -1) == 7)
+        assert c.max() <= 7
+
+
+def test_eight_bit_qmax():
+    y = np.array([[127.0, 63.5, -1.0, 0.2]])
+    codes, scales, _ = Q.quantize_groups(y, 4, "f32", bits=8)
+    assert float(scales[0, 0]) == 1.0
+    assert codes.tolist() == [[127, 64, -1, 0]]
+
+
+def test_pack_nibble_order():
+    assert Q.pack_int4(np.array([[1, -1]])).tolist() == [[0xF1]]
+    assert Q.pack_int4(np.array([[-7, 7]])).tolist() == [[0x79]]
+    assert Q.pack_int4(np.array([[0, -8, 3, 0]])).tolist() == [[0x80, 0x03]]
+
+
+def test_pack_unpack_round_trip_all_pairs():
+    v = np.arange(-8, 8)
+    pairs = np.array([[a, b] for a in v for b in v]).reshape(1, -1)
+    assert np.array_equal(Q.unpack_int4(Q.pack_int4(pairs)), pairs)
+    allbytes = np.arange(256, dtype=np.uint8).reshape(1, -1)
+    assert np.array_equal(Q.pack_int4(Q.unpack_int4(allbytes)), allbytes)
+
+
+def test_dequant_exact():
+    rng = np.random.default_rng(2)
+    codes = rng.integers(-7, 8, size=(4, 256)).astype(np.int8)
+    s16 = rng.uniform(0.001, 0.05, size=(4, 2)).astype(np.float16)
+    out = Q.dequant(codes, s16, 128)
+    exact = codes.reshape(4, 2, 128).astype(np.float64) * s16.astype(np.float64)[..., None]
+    assert np.array_equal(out.astype(np.float64), exact.reshape(4, 256))
+
+
+def test_quant_dequant_error_bound():
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((8, 512))
+    codes, scales, s_used = Q.quantize_groups(y, 64, "f16")
+    xh = Q.dequant(codes, scales, 64)
+    err = np.abs(xh - y.astype(np.float32)).reshape(8, 8, 64)
+    assert np.all(err <= 0.5 * s_used[..., None] * (1 + 1e-6))
+
+
+def test_rejects_group_not_dividing():
+    with pytest.raises(ValueError):
+        Q.quantize_groups(np.zeros((1, 10)), 4)
