@@ -1,0 +1,227 @@
+"""Throughput of the rotate / quantize / W4A4 path on one MI355X.
+
+One step = one fused randomized-Hadamard + int4 quantization pass
+(hr_rotate_quant_int4) over bf16 activations of 65536 tokens x 2048 channels,
+group 128, fp16 scales -- the workload the headline metric is quoted on.
+``value`` is that pass's throughput in GB/s of algorithmic bytes (input read
+once + codes and scales written once).  The W4A4 GEMM (4096^3 and M=16) and
+the other kernels are timed the same way and reported under ``kernels``.
+
+Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA peak
+METRIC = "fused RHT+int4 quant GB/s (% of HBM peak) at K=2048; W4A4 GEMM int8 TOPS"
+
+ROWS, N, GROUP = 65536, 2048, 128
+
+
+def rht_alg_bytes(rows, n, group, in_bytes=2, scale_bytes=2):
+    return rows * n * in_bytes + rows * n // 2 + rows * (n // group) * scale_bytes
+
+
+def _timed(fn, steps, warmup, nbuf=1):
+    """Run fn(i) warmup + steps times on the current stream; HIP events bracket
+    the timed launches.  Returns ms per call."""
+    import torch
+    for i in range(warmup):
+        fn(i % nbuf)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i % nbuf)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def cpu_baseline(target_s: float = 15.0):
+    """The oracle (fp64, explicit Hadamard matrix) on a bounded sample of the
+    same workload, on this host's cores."""
+    import hr_inputs
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    inp = hr_inputs.rht_inputs(rows=ROWS, n=N)
+    x = inp.x
+
+    def run(r0, r1):
+        y64 = oracle.hadamard.rht(x[r0:r1].float().numpy(), inp.signs)
+        codes, scales, _ = oracle.quant.quantize_groups(y64, GROUP, "f16")
+        oracle.quant.pack_int4(codes)
+
+    run(0, 512)                       # first call pays one-time costs
+    t0 = time.perf_counter()
+    run(0, 2048)
+    per_row = (time.perf_counter() - t0) / 2048
+    rows = int(min(ROWS, max(512, target_s / max(per_row, 1e-9))))
+    rows -= rows % 512
+    t0 = time.perf_counter()
+    for r0 in range(0, rows, 4096):
+        run(r0, min(rows, r0 + 4096))
+    dt = time.perf_counter() - t0
+    gbs = rht_alg_bytes(rows, N, GROUP) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {rows} of {ROWS} rows (bf16 x {N}, G={GROUP}, fp16 scales), "
+                      f"{dt:.1f} s wall, dense fp64 Hadamard matrix product + quantization"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-main", action="store_true", help="time only the headline kernel")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only (rows are independent; see DESIGN.md "
+              "for how it would shard); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import hr_inputs
+    import hadamard_rotation_int4_amd as hr
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- headline workload: 3 buffer sets (>= 1 GB) so consecutive steps do
+    # not hit in the 256 MB last-level cache
+    inp = hr_inputs.rht_inputs(rows=ROWS, n=N)
+    nbuf = 3
+    xs = [inp.x.to(dev) for _ in range(nbuf)]
+    d = torch.from_numpy(inp.signs).to(dev)
+    codes = [torch.empty((ROWS, N // 2), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    scales = [torch.empty((ROWS, N // GROUP), dtype=torch.float16, device=dev) for _ in range(nbuf)]
+
+    def step(i):
+        hr.rotate_quant_int4(xs[i], GROUP, d, codes=codes[i], scales=scales[i])
+
+    ms = _timed(step, args.steps, args.warmup, nbuf)
+    alg = rht_alg_bytes(ROWS, N, GROUP)
+    gbs = alg / (ms * 1e-3) / 1e9
+    kernels = {"rht_quant_bf16_65536x2048_g128": {"ms": ms, "GB/s": gbs,
+                                                  "frac_hbm": gbs / HBM_PEAK_GBS, "bytes": alg}}
+
+    if not args.only_main:
+        s32 = [torch.empty((ROWS, N // 32), dtype=torch.float16, device=dev) for _ in range(nbuf)]
+        ms32 = _timed(lambda i: hr.rotate_quant_int4(xs[i], 32, d, codes=codes[i], scales=s32[i]),
+                      args.steps, args.warmup, nbuf)
+        b32 = rht_alg_bytes(ROWS, N, 32)
+        kernels["rht_quant_bf16_65536x2048_g32"] = {"ms": ms32, "GB/s": b32 / ms32 / 1e6,
+                                                    "frac_hbm": b32 / ms32 / 1e6 / HBM_PEAK_GBS,
+                                                    "bytes": b32}
+        del s32
+        yf = torch.empty((ROWS, N), dtype=torch.float32, device=dev)
+        msr = _timed(lambda i: hr.rotate(xs[i], d, out=yf), args.steps, args.warmup, nbuf)
+        br = ROWS * N * 2 + ROWS * N * 4
+        kernels["rotate_bf16_to_f32_65536x2048"] = {"ms": msr, "GB/s": br / msr / 1e6,
+                                                    "frac_hbm": br / msr / 1e6 / HBM_PEAK_GBS,
+                                                    "bytes": br}
+        del yf
+        dq = torch.empty((ROWS, N), dtype=torch.float32, device=dev)
+        msd = _timed(lambda i: hr.dequant_int4(codes[i], scales[i], GROUP, out=dq),
+                     args.steps, args.warmup, nbuf)
+        bd = ROWS * N // 2 + ROWS * (N // GROUP) * 2 + ROWS * N * 4
+        kernels["dequant_int4_65536x2048_g128"] = {"ms": msd, "GB/s": bd / msd / 1e6,
+                                                   "frac_hbm": bd / msd / 1e6 / HBM_PEAK_GBS,
+                                                   "bytes": bd}
+        del dq
+        del xs, codes, scales
+
+        # mixed radix 16384 x (7*2048), G=128
+        mi = hr_inputs.mixed_inputs()
+        xm = mi.x.to(dev)
+        dm = torch.from_numpy(mi.signs).to(dev)
+        om = torch.from_numpy(mi.block).to(dev)
+        cm = torch.empty((mi.rows, mi.m * mi.p // 2), dtype=torch.uint8, device=dev)
+        sm = torch.empty((mi.rows, mi.m * mi.p // 128), dtype=torch.float16, device=dev)
+        msm = _timed(lambda i: hr.rotate_quant_int4(xm, 128, dm, om, codes=cm, scales=sm),
+                     max(5, args.steps // 2), 3)
+        bm = rht_alg_bytes(mi.rows, mi.m * mi.p, 128)
+        kernels["mixed_radix_quant_bf16_16384x14336_g128"] = {
+            "ms": msm, "GB/s": bm / msm / 1e6, "frac_hbm": bm / msm / 1e6 / HBM_PEAK_GBS, "bytes": bm}
+        del xm, cm, sm
+
+        # butterfly fp32 32768 x 4096 -> fp32, and fused G=64 quantization
+        bi = hr_inputs.butterfly_inputs()
+        xb = torch.from_numpy(bi.x).to(dev)
+        co = hr.butterfly_coeffs(torch.from_numpy(bi.angles).to(dev), False)
+        pb = torch.from_numpy(bi.perm).to(dev)
+        yb = torch.empty_like(xb)
+        msb = _timed(lambda i: hr.butterfly_apply(xb, co, False, pb, out=yb),
+                     max(5, args.steps // 2), 3)
+        bb = bi.rows * bi.n * 8
+        kernels["butterfly_f32_32768x4096"] = {"ms": msb, "GB/s": bb / msb / 1e6,
+                                               "frac_hbm": bb / msb / 1e6 / HBM_PEAK_GBS, "bytes": bb}
+        msbq = _timed(lambda i: hr.butterfly_apply(xb, co, False, pb, want_y=False, group=64),
+                      max(5, args.steps // 2), 3)
+        bbq = bi.rows * bi.n * 4 + bi.rows * bi.n // 2 + bi.rows * (bi.n // 64) * 2
+        kernels["butterfly_quant_f32_32768x4096_g64"] = {
+            "ms": msbq, "GB/s": bbq / msbq / 1e6, "frac_hbm": bbq / msbq / 1e6 / HBM_PEAK_GBS,
+            "bytes": bbq}
+        del xb, yb
+
+        # W4A4 GEMM 4096^3 and M=16, G=128
+        for M in (4096, 16):
+            gi = hr_inputs.gemm_inputs(M=M)
+            t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+            ad, sad, wd, swd = t(gi.a_codes), t(gi.a_scales), t(gi.w_codes), t(gi.w_scales)
+            cg = torch.empty((M, 4096), dtype=torch.float32, device=dev)
+            msg = _timed(lambda i: hr.w4a4_gemm(ad, sad, wd, swd, 128, out=cg), args.steps,
+                         args.warmup)
+            ops = 2 * M * 4096 * 4096
+            byts = M * 2048 + 4096 * 2048 + (M + 4096) * 32 * 2 + M * 4096 * 4
+            kernels[f"w4a4_gemm_{M}x4096x4096_g128"] = {
+                "ms": msg, "TOPS": ops / msg / 1e9, "frac_int8_peak": ops / msg / 1e9 / INT8_PEAK_TOPS,
+                "GB/s": byts / msg / 1e6, "ops": ops, "bytes": byts}
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "rotate_quant_int4: bf16 65536x2048 -> int4 codes + fp16 scales, "
+                               "G=128, seeded signs, 0.1% outlier channels x50",
+                   "rows": ROWS, "n": N, "group": GROUP},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    g4096 = kernels.get("w4a4_gemm_4096x4096x4096_g128")
+    if g4096:
+        out["w4a4_gemm_tops"] = round(g4096["TOPS"], 1)
+        out["w4a4_gemm_frac_int8_peak"] = round(g4096["frac_int8_peak"], 4)
+    out["kernels"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                      for k, v in kernels.items()}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

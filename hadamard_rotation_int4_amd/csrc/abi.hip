@@ -1,0 +1,244 @@
+// extern "C" entry points of libhr.so (declared in include/hr.h): host-side
+// argument validation, then a launch on the caller's stream.  A call that
+// fails validation makes no HIP call at all.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "hr.h"
+#include "hr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int32_t ok() { return HR_OK; }
+
+int32_t from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HR_EDEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+
+// Shared checks of hr_rotate and hr_rotate_quant_int4; fills p.
+int32_t check_rotation(const char* fn, const void* x, int32_t x_dtype, int64_t rows, int32_t n,
+                       int32_t m, const int8_t* signs, const float* block, int* p_out) {
+  if (rows < 0) return fail(HR_EINVAL, "%s: rows < 0", fn);
+  if (!x && rows > 0) return fail(HR_EINVAL, "%s: x is NULL", fn);
+  if (x_dtype != HR_BF16 && x_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: x_dtype must be HR_BF16 or HR_F32", fn);
+  if (!aligned16(x) || (signs && !aligned16(signs)))
+    return fail(HR_EINVAL, "%s: x and signs must be 16-byte aligned", fn);
+  if (m < 1 || m > 16) return fail(HR_EUNSUPPORTED, "%s: m=%d outside [1, 16]", fn, m);
+  if (n <= 0 || n % m) return fail(HR_EUNSUPPORTED, "%s: n=%d is not a multiple of m=%d", fn, n, m);
+  const int p = n / m;
+  if (!pow2(p) || p < 64 || p > 16384)
+    return fail(HR_EUNSUPPORTED, "%s: n/m=%d is not a power of two in [64, 16384]", fn, p);
+  if (n > 16384) return fail(HR_EUNSUPPORTED, "%s: n=%d > 16384", fn, n);
+  if (m == 1 && block) return fail(HR_EINVAL, "%s: block must be NULL when m == 1", fn);
+  if (m > 1 && !block) return fail(HR_EINVAL, "%s: block is NULL with m=%d", fn, m);
+  if (block && (reinterpret_cast<uintptr_t>(block) & 3u))
+    return fail(HR_EINVAL, "%s: block must be 4-byte aligned", fn);
+  *p_out = p;
+  return HR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t hr_abi_version(void) { return HR_ABI_VERSION; }
+
+const char* hr_status_string(int32_t status) {
+  switch (status) {
+    case HR_OK: return "HR_OK: success";
+    case HR_EINVAL: return "HR_EINVAL: invalid argument";
+    case HR_EUNSUPPORTED: return "HR_EUNSUPPORTED: size or mode not supported";
+    case HR_EDEVICE: return "HR_EDEVICE: kernel launch failed";
+    default: return "unknown hr_status";
+  }
+}
+
+const char* hr_last_error(void) { return g_last_error.c_str(); }
+
+int32_t hr_rotate(const void* x, int32_t x_dtype, float* y, int64_t rows, int32_t n, int32_t m,
+                  const int8_t* signs, const float* block, void* stream) {
+  int p = 0;
+  const int32_t st = check_rotation("hr_rotate", x, x_dtype, rows, n, m, signs, block, &p);
+  if (st) return st;
+  if (!y && rows > 0) return fail(HR_EINVAL, "hr_rotate: y is NULL");
+  if (!aligned16(y)) return fail(HR_EINVAL, "hr_rotate: y must be 16-byte aligned");
+  if (rows == 0) return ok();
+  hr::RhtArgs a{};
+  a.x = x;
+  a.x_bf16 = x_dtype == HR_BF16;
+  a.rows = rows;
+  a.n = n;
+  a.m = m;
+  a.p = p;
+  a.signs = signs;
+  a.block = block;
+  a.y = y;
+  return from_hip(hr::launch_rht(a, static_cast<hipStream_t>(stream)), "hr_rotate");
+}
+
+int32_t hr_rotate_quant_int4(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t m,
+                             const int8_t* signs, const float* block, int32_t group,
+                             uint8_t* codes, void* scales, int32_t scale_dtype, void* stream) {
+  int p = 0;
+  const char* fn = "hr_rotate_quant_int4";
+  const int32_t st = check_rotation(fn, x, x_dtype, rows, n, m, signs, block, &p);
+  if (st) return st;
+  if ((!codes || !scales) && rows > 0)
+    return fail(HR_EINVAL, "%s: codes and scales are required", fn);
+  if (!aligned16(codes) || !aligned16(scales))
+    return fail(HR_EINVAL, "%s: codes and scales must be 16-byte aligned", fn);
+  if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+  if (!valid_group(group)) return fail(HR_EUNSUPPORTED, "%s: group=%d not in {32,64,128,256}", fn, group);
+  if (p % group) return fail(HR_EUNSUPPORTED, "%s: group=%d does not divide p=%d", fn, group, p);
+  if (rows == 0) return ok();
+  hr::RhtArgs a{};
+  a.x = x;
+  a.x_bf16 = x_dtype == HR_BF16;
+  a.rows = rows;
+  a.n = n;
+  a.m = m;
+  a.p = p;
+  a.signs = signs;
+  a.block = block;
+  a.group = group;
+  a.codes = codes;
+  a.scales = scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  return from_hip(hr::launch_rht(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t hr_butterfly_coeffs(const float* angles, int32_t n, int32_t precondition, float* coeffs,
+                            void* stream) {
+  const char* fn = "hr_butterfly_coeffs";
+  if (!angles || !coeffs) return fail(HR_EINVAL, "%s: angles and coeffs are required", fn);
+  if (!aligned16(angles) || !aligned16(coeffs))
+    return fail(HR_EINVAL, "%s: angles and coeffs must be 16-byte aligned", fn);
+  if (precondition != 0 && precondition != 1) return fail(HR_EINVAL, "%s: precondition must be 0 or 1", fn);
+  if (!pow2(n) || n < 64 || n > 8192)
+    return fail(HR_EUNSUPPORTED, "%s: n=%d is not a power of two in [64, 8192]", fn, n);
+  return from_hip(hr::launch_butterfly_coeffs(angles, n, ilog2(n), precondition, coeffs,
+                                              static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t hr_butterfly_apply(const float* x, float* y, int64_t rows, int32_t n, const float* coeffs,
+                           int32_t precondition, const int32_t* perm, int32_t inverse,
+                           int32_t group, uint8_t* codes, void* scales, int32_t scale_dtype,
+                           void* stream) {
+  const char* fn = "hr_butterfly_apply";
+  if (rows < 0) return fail(HR_EINVAL, "%s: rows < 0", fn);
+  if (!coeffs) return fail(HR_EINVAL, "%s: coeffs is required", fn);
+  if (!x && rows > 0) return fail(HR_EINVAL, "%s: x is NULL", fn);
+  if (!y && !codes && rows > 0) return fail(HR_EINVAL, "%s: y and codes are both NULL", fn);
+  if (!codes && scales) return fail(HR_EINVAL, "%s: scales given without codes", fn);
+  if (codes && !scales) return fail(HR_EINVAL, "%s: codes given without scales", fn);
+  if (!aligned16(x) || (y && !aligned16(y)) || !aligned16(coeffs) || (perm && !aligned16(perm)) ||
+      (codes && !aligned16(codes)) || (scales && !aligned16(scales)))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (precondition != 0 && precondition != 1) return fail(HR_EINVAL, "%s: precondition must be 0 or 1", fn);
+  if (inverse != 0 && inverse != 1) return fail(HR_EINVAL, "%s: inverse must be 0 or 1", fn);
+  if (!pow2(n) || n < 64 || n > 8192)
+    return fail(HR_EUNSUPPORTED, "%s: n=%d is not a power of two in [64, 8192]", fn, n);
+  if (codes) {
+    if (inverse) return fail(HR_EUNSUPPORTED, "%s: quantization needs inverse == 0", fn);
+    if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+      return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+    if (!valid_group(group) || n % group)
+      return fail(HR_EUNSUPPORTED, "%s: group=%d invalid for n=%d", fn, group, n);
+  }
+  if (rows == 0) return ok();
+  hr::ButterflyArgs a{};
+  a.x = x;
+  a.y = y;
+  a.rows = rows;
+  a.n = n;
+  a.log2n = ilog2(n);
+  a.coeffs = coeffs;
+  a.precondition = precondition;
+  a.perm = perm;
+  a.inverse = inverse;
+  a.group = group;
+  a.codes = codes;
+  a.scales = scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  return from_hip(hr::launch_butterfly(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t hr_dequant_int4(const uint8_t* codes, const void* scales, int32_t scale_dtype, int64_t rows,
+                        int32_t n, int32_t group, float* out, void* stream) {
+  const char* fn = "hr_dequant_int4";
+  if (rows < 0) return fail(HR_EINVAL, "%s: rows < 0", fn);
+  if ((!codes || !scales || !out) && rows > 0)
+    return fail(HR_EINVAL, "%s: codes, scales and out are required", fn);
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(out))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+  if (!valid_group(group)) return fail(HR_EUNSUPPORTED, "%s: group=%d not in {32,64,128,256}", fn, group);
+  if (n <= 0 || n % group || n > (1 << 30))
+    return fail(HR_EUNSUPPORTED, "%s: n=%d must be a positive multiple of group=%d", fn, n, group);
+  if (rows == 0) return ok();
+  return from_hip(hr::launch_dequant(codes, scales, scale_dtype == HR_F16, rows, n, group, out,
+                                     static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales, const uint8_t* w_codes,
+                     const void* w_scales, int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
+                     int32_t group, float* c, int32_t* group_acc, void* stream) {
+  const char* fn = "hr_w4a4_gemm";
+  if (M < 0 || N < 0 || K < 0) return fail(HR_EINVAL, "%s: negative size", fn);
+  if (M > 0 && N > 0 && (!a_codes || !a_scales || !w_codes || !w_scales || !c))
+    return fail(HR_EINVAL, "%s: a_codes, a_scales, w_codes, w_scales and c are required", fn);
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(c) || (group_acc && !aligned16(group_acc)))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+  if (group != 64 && group != 128 && group != 256)
+    return fail(HR_EUNSUPPORTED, "%s: group=%d not in {64,128,256}", fn, group);
+  if (N % 64) return fail(HR_EUNSUPPORTED, "%s: N=%lld is not a multiple of 64", fn, (long long)N);
+  if (K == 0 || K % 256 || K % group || K > 65536)
+    return fail(HR_EUNSUPPORTED, "%s: K=%lld must be a multiple of 256 and of group, <= 65536", fn,
+                (long long)K);
+  if (M == 0 || N == 0) return ok();
+  hr::GemmArgs a{};
+  a.a = a_codes;
+  a.sa = a_scales;
+  a.w = w_codes;
+  a.sw = w_scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.group = group;
+  a.c = c;
+  a.group_acc = group_acc;
+  return from_hip(hr::launch_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

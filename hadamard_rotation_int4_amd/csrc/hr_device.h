@@ -1,0 +1,53 @@
+// Device helpers shared by the kernels of libhr.so (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hr {
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_float(const T* p);
+
+template <>
+__device__ __forceinline__ float load_as_float<float>(const float* p) { return *p; }
+
+template <>
+__device__ __forceinline__ float load_as_float<uint16_t>(const uint16_t* p) {
+  return bf16_bits_to_float(*p);
+}
+
+// Store a group scale in the caller's scale dtype; returns the value the codes
+// must be taken against (the stored one, widened to fp32).
+__device__ __forceinline__ float store_scale(void* scales, int64_t idx, float s32, int scale_f16) {
+  if (scale_f16) {
+    _Float16 h = (_Float16)s32;  // v_cvt_f16_f32: round to nearest even
+    reinterpret_cast<_Float16*>(scales)[idx] = h;
+    return (float)h;
+  }
+  reinterpret_cast<float*>(scales)[idx] = s32;
+  return s32;
+}
+
+// Reference-style code of one value: round half away from zero, clamp to +-7,
+// zero for a zero scale.  Used by the straightforward kernels.
+__device__ __forceinline__ int quant_code_exact(float y, float s) {
+  if (s == 0.0f) return 0;
+  float t = y / s;                       // IEEE division
+  float a = floorf(fabsf(t) + 0.5f);     // exact for |t| < 2^22
+  a = fminf(a, 7.0f);
+  int q = (int)a;
+  return t < 0.0f ? -q : q;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace hr

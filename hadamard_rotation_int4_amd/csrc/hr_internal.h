@@ -1,0 +1,60 @@
+// Internal declarations shared by the HIP translation units of libhr.so.
+// Nothing here is part of the public ABI (include/hr.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hr {
+
+// Arguments of one rotate / rotate+quantize call after host validation.
+struct RhtArgs {
+  const void* x;
+  int x_bf16;            // 1: bf16 input, 0: fp32 input
+  int64_t rows;
+  int n, m, p;           // n = m * p
+  const int8_t* signs;   // may be null (all +1)
+  const float* block;    // [m][m], null when m == 1
+  float* y;              // fp32 output or null
+  int group;             // quantization group (when codes != null)
+  uint8_t* codes;        // packed int4 output or null
+  void* scales;          // scale output or null
+  int scale_f16;         // 1: fp16 scales, 0: fp32 scales
+};
+
+struct ButterflyArgs {
+  const float* x;
+  float* y;
+  int64_t rows;
+  int n, log2n;
+  const float* coeffs;   // [log2 n][n/2][2]
+  int precondition;
+  const int* perm;
+  int inverse;
+  int group;
+  uint8_t* codes;
+  void* scales;
+  int scale_f16;
+};
+
+struct GemmArgs {
+  const uint8_t* a;
+  const void* sa;
+  const uint8_t* w;
+  const void* sw;
+  int scale_f16;
+  int64_t M, N, K;
+  int group;
+  float* c;
+  int32_t* group_acc;
+};
+
+hipError_t launch_rht(const RhtArgs& a, hipStream_t s);
+hipError_t launch_butterfly_coeffs(const float* angles, int n, int log2n, int precondition,
+                                   float* coeffs, hipStream_t s);
+hipError_t launch_butterfly(const ButterflyArgs& a, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const void* scales, int scale_f16, int64_t rows,
+                          int n, int group, float* out, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace hr

@@ -1,0 +1,228 @@
+/*
+ * hr.h -- C ABI of libhr.so: randomized Hadamard rotation, fused int4
+ * quantization, HARP-style butterfly, int4 dequant and the W4A4 GEMM on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array argument is a DEVICE pointer owned by the caller; the library
+ *   allocates no memory and keeps no state between calls.
+ * - Every call is asynchronous: it enqueues kernels on `stream` (a
+ *   hipStream_t; NULL means the null stream) and returns.  Buffers must stay
+ *   valid until the stream has executed the work.
+ * - Arguments are validated on the host before anything is enqueued.  A call
+ *   that returns an error has enqueued nothing and made no HIP call:
+ *     HR_EINVAL        null pointer where one is required, negative size,
+ *                      pointer not 16-byte aligned, unknown dtype code;
+ *     HR_EUNSUPPORTED  a size or mode outside what the kernels implement;
+ *     HR_EDEVICE       the kernel launch itself failed (hipGetLastError).
+ *   hr_last_error() returns a message describing the most recent failure of
+ *   the calling thread.
+ * - rows == 0 (or M == 0 or N == 0) is a valid no-op that returns HR_OK once
+ *   the scalar arguments are valid; the arrays sized by it may then be NULL.
+ * - Calls are thread-safe; concurrent calls on different streams are fine.
+ * - Rows are contiguous and row-major: row r of an [rows][n] array starts at
+ *   element r*n.
+ * - int4 codes are packed two per byte, two's complement, element 2j in the
+ *   low nibble and element 2j+1 in the high nibble; the quantizer produces
+ *   codes in [-7, 7] only.
+ *
+ * Notation: x a row of length n; d a +-1 sign diagonal; H_p the Sylvester-
+ * Hadamard matrix of order p = 2^k in natural order, H[i][j] =
+ * (-1)^popcount(i & j); O an m x m orthogonal block; G the group size.
+ */
+#ifndef HR_H
+#define HR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HR_OK = 0,
+  HR_EINVAL = 1,
+  HR_EUNSUPPORTED = 2,
+  HR_EDEVICE = 3
+} hr_status;
+
+typedef enum {
+  HR_F32 = 0,   /* IEEE binary32 */
+  HR_BF16 = 1,  /* bfloat16 */
+  HR_F16 = 2    /* IEEE binary16 */
+} hr_dtype;
+
+/* ABI version of this header (bumped on any signature change). */
+#define HR_ABI_VERSION 1
+int32_t hr_abi_version(void);
+
+/* Static description of a status code. */
+const char* hr_status_string(int32_t status);
+
+/* Message of the calling thread's most recent failed call ("" if none). */
+const char* hr_last_error(void);
+
+/*
+ * hr_rotate -- randomized (mixed-radix) Hadamard rotation, fp32 output.
+ *
+ * Defines: "Experiment -- Hadamard rotation for int4 (W4A4) accuracy",
+ * Hypothesis and Method (Q = H / sqrt(K) applied by a fast Walsh-Hadamard
+ * transform then x 1/sqrt(K)); HARP abstract (the fixed randomized Hadamard
+ * transform of incoherence processing; mixed-radix schedules for dimensions
+ * that are not powers of two); HARP technical summary, section 2.1 (a radix
+ * that is not a power of two uses a fixed orthogonal block).
+ *
+ * For every row r:   y[r] = (O kron H_p) (d * x[r]) / sqrt(p),   n = m * p,
+ * with (O kron H)[i*p+a][j*p+b] = O[i][j] H[a][b] (chunk i of a row is elements
+ * [i*p, (i+1)*p)).  m == 1 is the plain randomized Hadamard transform
+ * y = H_n (d * x) / sqrt(n).
+ *
+ *   x       [rows][n] of x_dtype (HR_BF16 or HR_F32).
+ *   y       [rows][n] fp32.  y == x is allowed when x_dtype == HR_F32
+ *           (in place); any other overlap is undefined.
+ *   n       row length, n = m * p with p a power of two, 64 <= p <= 16384,
+ *           and n <= 16384.
+ *   m       number of chunks, 1 <= m <= 16.
+ *   signs   [n] int8, each +1 or -1 (other values are undefined behaviour);
+ *           NULL means all +1.
+ *   block   [m][m] fp32 row-major orthogonal block O; must be NULL when
+ *           m == 1 and non-NULL when m > 1.  It is used as given (it is not
+ *           re-orthogonalised).
+ */
+int32_t hr_rotate(const void* x, int32_t x_dtype, float* y, int64_t rows,
+                  int32_t n, int32_t m, const int8_t* signs, const float* block,
+                  void* stream);
+
+/*
+ * hr_rotate_quant_int4 -- hr_rotate fused with per-group symmetric absmax int4
+ * quantization and nibble packing.  The rotated values never leave the chip.
+ *
+ * Defines: as hr_rotate, plus "Experiment -- Hadamard rotation for int4 (W4A4)
+ * accuracy", Method (per-group symmetric integer quantize/dequantize) and
+ * Verdict (per-group work belongs inside one kernel).
+ *
+ * For every row and every group of G consecutive rotated values y (aligned at
+ * multiples of G):
+ *   a   = max |y| over the group           (fp32)
+ *   s32 = a / 7                             (fp32)
+ *   s   = s32 rounded to fp16 (scale_dtype HR_F16) or s32 (HR_F32); stored
+ *   q   = y / s rounded to nearest, clamped to [-7, 7]; 0 when s == 0.
+ * Rounding ties of y / s are resolved to even; results within 1e-4 of a tie
+ * may differ from a round-half-away reference.
+ *
+ *   codes   [rows][n/2] uint8, packed int4 (see conventions).
+ *   scales  [rows][n/G] of scale_dtype (HR_F16 or HR_F32).
+ *   group   G in {32, 64, 128, 256}; G must divide p.
+ *   other arguments as hr_rotate.
+ */
+int32_t hr_rotate_quant_int4(const void* x, int32_t x_dtype, int64_t rows,
+                             int32_t n, int32_t m, const int8_t* signs,
+                             const float* block, int32_t group, uint8_t* codes,
+                             void* scales, int32_t scale_dtype, void* stream);
+
+/*
+ * hr_butterfly_coeffs -- build the per-pair 2x2 coefficient table of a
+ * HARP-style butterfly from its angles (run once per set of angles).
+ *
+ * Defines: HARP technical summary, section 2.2: block kernel
+ * B(theta) = Q(theta) G_b with Q a Givens rotation for b = 2 and G_2 the
+ * normalised Sylvester-Hadamard mixer; theta = 0 gives B = G_2.
+ *
+ * Stage s (0 <= s < log2 n) pairs elements (i, i + 2^s) for every i with bit s
+ * clear; the pair's index is ((i >> (s+1)) << s) | (i & (2^s - 1)).  For pair
+ * index j of stage s, with c = cos(angles[s][j]), t = sin(angles[s][j])
+ * evaluated in double precision:
+ *   precondition == 0:  block [[c, -t], [t, c]]          -> stores (c, t)
+ *   precondition == 1:  block [[c, -t], [t, c]] G_2
+ *                       = [[u, v], [v, -u]], u = (c - t)/sqrt2,
+ *                         v = (c + t)/sqrt2                -> stores (u, v)
+ *   angles  [log2 n][n/2] fp32.
+ *   coeffs  [log2 n][n/2][2] fp32 (output; pass it to hr_butterfly_apply with
+ *           the same precondition value).
+ *   n       power of two, 64 <= n <= 8192.
+ */
+int32_t hr_butterfly_coeffs(const float* angles, int32_t n, int32_t precondition,
+                            float* coeffs, void* stream);
+
+/*
+ * hr_butterfly_apply -- apply the butterfly (or its transpose) to every row,
+ * optionally fused with int4 quantization of the result.
+ *
+ * Defines: HARP abstract (a rotation as a product of sparse butterfly-like
+ * block-orthogonal stages); HARP technical summary, sections 2.1 (stages of
+ * block-diagonal orthogonal matrices separated by stride permutations; here the
+ * permutations are folded into the pair indexing), 2.2 (the block kernel) and
+ * 2.4 (O(d log d) application without materialised permutations).
+ *
+ * Forward (inverse == 0): stages s = 0 .. log2(n)-1 in ascending order, each
+ * block applied to (x_i, x_{i+2^s}) as a column vector, then the gather
+ * y[i] = z[perm[i]].  Inverse (inverse == 1): the transpose: scatter
+ * z[perm[i]] = x[i], then the transposed blocks in descending stage order.
+ *
+ *   x       [rows][n] fp32.
+ *   y       [rows][n] fp32 output, or NULL to skip the fp32 output.  y == x is
+ *           allowed (in place).
+ *   coeffs  table from hr_butterfly_coeffs for the same n and precondition.
+ *   precondition  0 or 1, as given to hr_butterfly_coeffs.
+ *   perm    [n] int32 permutation of 0..n-1; NULL means identity.
+ *   codes, scales, group, scale_dtype: as hr_rotate_quant_int4, quantizing
+ *           the butterfly output; codes == NULL skips quantization (then
+ *           scales must be NULL too).  At least one of y and codes must be
+ *           non-NULL.  Quantization is only available with inverse == 0.
+ */
+int32_t hr_butterfly_apply(const float* x, float* y, int64_t rows, int32_t n,
+                           const float* coeffs, int32_t precondition,
+                           const int32_t* perm, int32_t inverse, int32_t group,
+                           uint8_t* codes, void* scales, int32_t scale_dtype,
+                           void* stream);
+
+/*
+ * hr_dequant_int4 -- x_hat = q * s per element (one fp32 product, so the result
+ * is bit-exact).
+ *
+ * Defines: "Experiment -- Hadamard rotation for int4 (W4A4) accuracy", Method
+ * (quantize -> dequantize).
+ *
+ *   codes   [rows][n/2] uint8 packed int4.
+ *   scales  [rows][n/G] of scale_dtype (HR_F16 or HR_F32).
+ *   n       even, a multiple of G, n <= 2^30.
+ *   group   G in {32, 64, 128, 256}.
+ *   out     [rows][n] fp32.
+ */
+int32_t hr_dequant_int4(const uint8_t* codes, const void* scales,
+                        int32_t scale_dtype, int64_t rows, int32_t n,
+                        int32_t group, float* out, void* stream);
+
+/*
+ * hr_w4a4_gemm -- C = A W^T on packed int4 operands with per-group scales.
+ *
+ * Defines: "Experiment -- Hadamard rotation for int4 (W4A4) accuracy",
+ * Hypothesis (W4A4: both operands int4 on a same-precision integer MAC) and
+ * Verdict (the per-group scaling must stay inside one GEMM).
+ *
+ *   acc[m][n][g] = sum_{k = gG}^{gG+G-1} A[m][k] W[n][k]      (exact int32)
+ *   C[m][n]      = sum_g sA[m][g] sW[n][g] acc[m][n][g]       (fp32)
+ *
+ *   a_codes   [M][K/2] uint8 packed int4 (activations, K contiguous).
+ *   a_scales  [M][K/G] of scale_dtype.
+ *   w_codes   [N][K/2] uint8 packed int4 (weights, K contiguous).
+ *   w_scales  [N][K/G] of scale_dtype.
+ *   scale_dtype  HR_F16 or HR_F32.
+ *   M >= 0; N a multiple of 64; K a multiple of 256 and of G, K <= 65536.
+ *   group     G in {64, 128, 256}.
+ *   c         [M][N] fp32 output.
+ *   group_acc optional [M][N][K/G] int32 output of the exact per-group sums
+ *             (a debugging aid; NULL to skip).
+ * Codes equal to -8 are accepted and multiply exactly.
+ */
+int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales,
+                     const uint8_t* w_codes, const void* w_scales,
+                     int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
+                     int32_t group, float* c, int32_t* group_acc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HR_H */
