@@ -122,6 +122,7 @@ __global__ __launch_bounds__(256) void w4a4_gemm_simple_kernel(GemmArgs g) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (launch_gemm_mfma(a, s)) return hipGetLastError();
   const dim3 grid((unsigned)(a.N / kTile), (unsigned)((a.M + kTile - 1) / kTile));
   if (a.scale_f16)
     hipLaunchKernelGGL(w4a4_gemm_simple_kernel<true>, grid, dim3(256), 0, s, a);

@@ -57,5 +57,6 @@ hipError_t launch_butterfly(const ButterflyArgs& a, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int scale_f16, int64_t rows,
                           int n, int group, float* out, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+bool launch_gemm_mfma(const GemmArgs& a, hipStream_t s);  // false: not handled
 
 }  // namespace hr

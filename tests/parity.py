@@ -92,7 +92,12 @@ def check_quant(codes_gpu, scales_gpu, y64, group, scale_mode="f16"):
 
 def check_gemm(c_gpu, c_ref, bound, acc_gpu=None, acc_ref=None):
     if acc_gpu is not None:
-        assert np.array_equal(np.asarray(acc_gpu, dtype=np.int64), acc_ref), "group sums differ"
+        a = np.asarray(acc_gpu, dtype=np.int64)
+        bad = a != acc_ref
+        assert not bad.any(), (f"{bad.sum()} of {bad.size} group sums differ; first "
+                               f"[m, n, g] {np.argwhere(bad)[:4].tolist()}, gpu "
+                               f"{a[bad][:4].tolist()} oracle {acc_ref[bad][:4].tolist()}; "
+                               f"rows with errors {np.unique(np.argwhere(bad)[:, 0])[:12].tolist()}")
     err = np.abs(np.asarray(c_gpu, dtype=np.float64) - c_ref.astype(np.float64))
     ok = err <= GEMM_REL * bound + 1e-30
     assert ok.all(), f"{(~ok).sum()} outputs beyond 1e-5 relative; worst {(err / bound).max():.3g}"
