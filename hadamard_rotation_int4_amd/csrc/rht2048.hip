@@ -1,159 +1,28 @@
-// Randomized Hadamard transform of length-2048 rows fused with int4
-// quantization: one wave64 per row, the whole row in registers.
+// Randomized Hadamard transform of rows built from 2048-point chunks, fused
+// with int4 quantization (or an fp32 store).  The chunk transform itself is
+// the register-resident wave64 routine of fwht2048.h.
 //
-// What is computed (same as the general kernel): y = H_2048 (d * x) / sqrt(2048)
-// ("Experiment -- Hadamard rotation for int4 (W4A4) accuracy", Hypothesis and
-// Method; the 2048-point Hadamard of the "Llama-3.2-1B-Instruct-HadamardSpin-
-// 4bits" card, How it Works), then per-group absmax int4 codes (same experiment
-// page, Method).
+// rht2048_kernel: n = 2048 ("Experiment -- Hadamard rotation for int4 (W4A4)
+//   accuracy", Hypothesis and Method; "Llama-3.2-1B-Instruct-HadamardSpin-
+//   4bits", How it Works).  One wave per row, persistent over rows, the next
+//   row's loads in flight while the current one is transformed.
 //
-// Data placement.  Lane l loads bf16 elements j*512 + 8l + e (j < 4, e < 8)
-// with four 16-byte loads, so element-index bits 0-2 (e) and 9-10 (j) live in
-// registers and bits 3-8 live in lane bits 0-5.  The Walsh-Hadamard butterfly
-// over a bit never moves data, so the stages run in any order:
-//   bit 0        v_dot2_f32_bf16 of the packed bf16 pair against (d0, +-d1):
-//                widening, sign diagonal and first butterfly in one op;
-//   bits 1,2,9,10  register butterflies;
-//   bit 8        v_permlane32_swap exchanges lane bit 5 with register bit j1
-//                (already transformed), then a register butterfly;
-//   bit 7        v_permlane16_swap exchanges lane bit 4 with register bit j0;
-//   bits 3-6     lane bits 0-3, one v_fmac_f32_dpp each (partner through DPP,
-//                per-lane +-1 multiplier).  DPP offers lane xor 1, 2 (quad_perm),
-//                7 (row_half_mirror) and 8 (row_ror:8) but no xor 4, so within
-//                each 16-lane row the lanes are relabelled by a GF(2)-linear map:
-//                logical index a = (a0, a1, a2, a3) sits in physical lane
-//                q = a0*1 ^ a1*2 ^ a2*7 ^ a3*8, making logical bit 2 physical
-//                xor 7.  The loads stay coalesced (a permutation of 16 lanes).
-//                Lane sign bookkeeping: the fmac computes own + beta * partner,
-//                which is the butterfly up to a per-lane sign tau that depends
-//                only on the transformed bits; tau = (-1)^popcount(a) at the end
-//                and is folded into the output multiplier.
-// Final placement: element e | a << 3 | j0 << 7 | j1 << 8 | (l >> 4) << 9.
-// A quantization group of 128 is then 8 registers x one 16-lane row, 32 is 8
-// registers x a quad, 64 is 8 registers x 8 lanes, 256 spans j0 too.
+// mixed2048_kernel: n = m * 2048, y = (O kron H_2048) D x / sqrt(2048) (HARP
+//   abstract: mixed-radix schedules for dimensions that are not powers of two;
+//   HARP technical summary (gist.science), section 2.1: a radix that is not a
+//   power of two uses a fixed orthogonal block).  One workgroup of m waves per
+//   row: wave w transforms chunk w in registers and writes it to LDS; after a
+//   barrier wave w forms output chunk w = sum_c O[w][c] * chunk_c from LDS (m
+//   fma per element, same register placement) and quantizes or stores it.
 #include "hr_internal.h"
-#include "hr_device.h"
+#include "fwht2048.h"
 
-// Persistent grid: blocks of 4 waves per compute unit (256 CUs).
+// Persistent grid of the row kernel: blocks of 4 waves per compute unit.
 #ifndef HR_RHT2048_BLOCKS_PER_CU
-#define HR_RHT2048_BLOCKS_PER_CU 4
+#define HR_RHT2048_BLOCKS_PER_CU 8
 #endif
 
 namespace hr {
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
-}
-
-// DPP controls
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-
-// w[i] += dpp(w[i]) * sigma for 16 registers.  All 16 are operands of one
-// asm block that opens with s_nop 1, so every VALU write of them has retired
-// at least two wait states before its DPP read.
-#define HR_FMAC_DPP16(w, sigma, CTRL) \
-  asm volatile("s_nop 1\n\t" \
-"v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-"v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
-  : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4]), "+v"(w[5]), "+v"(w[6]), "+v"(w[7]), "+v"(w[8]), "+v"(w[9]), "+v"(w[10]), "+v"(w[11]), "+v"(w[12]), "+v"(w[13]), "+v"(w[14]), "+v"(w[15]) \
-  : "v"(sigma))
-
-__device__ __forceinline__ void bfly(float& a, float& b) {
-  const float t = a;
-  a = t + b;
-  b = t - b;
-}
-
-// v_dot2_f32_bf16 in its VOP3P form (separate accumulator, sign modifiers on
-// the halves of the second operand): d = x.lo * s.lo + x.hi * s.hi + c.
-__device__ __forceinline__ float dot2_pp(uint32_t x, uint32_t s) {  // ( s.lo,  s.hi) + 0
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(x), "v"(s));
-  return d;
-}
-__device__ __forceinline__ float dot2_pm(uint32_t x, uint32_t s) {  // ( s.lo, -s.hi) + 0
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(d) : "v"(x), "v"(s));
-  return d;
-}
-__device__ __forceinline__ float dot2_pp_c(uint32_t x, uint32_t s, float c) {  // ( s.lo,  s.hi) + c
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(x), "v"(s), "v"(c));
-  return d;
-}
-__device__ __forceinline__ float dot2_pm_c(uint32_t x, uint32_t s, float c) {  // ( s.lo, -s.hi) + c
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3 neg_hi:[0,1,0]" : "=v"(d) : "v"(x), "v"(s), "v"(c));
-  return d;
-}
-__device__ __forceinline__ float dot2_mm_c(uint32_t x, uint32_t s, float c) {  // (-s.lo, -s.hi) + c
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3 neg_lo:[0,1,0] neg_hi:[0,1,0]" : "=v"(d) : "v"(x), "v"(s), "v"(c));
-  return d;
-}
-__device__ __forceinline__ float dot2_mp_c(uint32_t x, uint32_t s, float c) {  // (-s.lo,  s.hi) + c
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3 neg_lo:[0,1,0]" : "=v"(d) : "v"(x), "v"(s), "v"(c));
-  return d;
-}
-
-// Max over lanes of non-negative fp32 values, compared as unsigned bit
-// patterns (same order for non-negative floats, and no NaN canonicalisation).
-template <int CTRL>
-__device__ __forceinline__ uint32_t umax_dpp(uint32_t a) {
-  const uint32_t b = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, CTRL, 0xf, 0xf, true);
-  return a > b ? a : b;
-}
-
-template <int CTRL>
-__device__ __forceinline__ float qbcast(float v) { return dpp<CTRL>(v); }
-
-// Correctly rounded fp32 a / 7 (one residual correction of a * RN(1/7)).
-__device__ __forceinline__ float div7(float a) {
-  const float r7 = 1.0f / 7.0f;
-  const float q0 = a * r7;
-  const float r = fmaf(-q0, 7.0f, a);
-  return fmaf(r, r7, q0);
-}
-
-// Pack 8 codes held as magic-rounded floats (bits = 0x4B400008 + q, so the
-// low byte is q + 8 in [1, 15] with clean high nibble) into one dword of
-// two's-complement nibbles, element 0 in the low nibble.
-__device__ __forceinline__ uint32_t pack8(const float* r) {
-  uint32_t u[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) u[e] = __float_as_uint(r[e]);
-  const uint32_t p01 = (u[1] << 4) | u[0];
-  const uint32_t p23 = (u[3] << 4) | u[2];
-  const uint32_t p45 = (u[5] << 4) | u[4];
-  const uint32_t p67 = (u[7] << 4) | u[6];
-  const uint32_t lo = (p23 << 8) | p01;      // bits 0-15 clean
-  const uint32_t hi = (p67 << 8) | p45;
-  const uint32_t w = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-  return w ^ 0x88888888u;
-}
 
 template <bool IN_BF16, int G, bool SCALE_F16, bool OUT_F32>
 __global__ __launch_bounds__(256) void rht2048_kernel(const void* __restrict__ xin,
@@ -162,46 +31,13 @@ __global__ __launch_bounds__(256) void rht2048_kernel(const void* __restrict__ x
                                                        uint8_t* __restrict__ codes,
                                                        void* __restrict__ scales, float norm) {
   constexpr int N = 2048;
-  const int lane = threadIdx.x & 63;
-  // logical index of this lane within its 16-lane row (see header)
-  const int q = lane & 15;
-  const int a4 = (q & 12) | ((q ^ (q >> 2)) & 1) | ((((q >> 1) ^ (q >> 2)) & 1) << 1);
-  const int lg = (lane & 48) | a4;   // logical lane: element bits 3-8 at load time
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  Lane2048 L;
+  lane2048_init(L, signs);
 
-  // sign pairs (bf16 +-1, +-1) for elements j*512 + 8*lane + 2k, +1
-  uint32_t sp[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (signs) {
-      const uint2 s8 = *reinterpret_cast<const uint2*>(signs + j * 512 + 8 * lg);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w = k < 2 ? s8.x : s8.y;
-        const int b0 = (int8_t)((w >> (16 * (k & 1))) & 0xFF);
-        const int b1 = (int8_t)((w >> (16 * (k & 1) + 8)) & 0xFF);
-        sp[j][k] = (b0 < 0 ? 0xBF80u : 0x3F80u) | ((b1 < 0 ? 0xBF80u : 0x3F80u) << 16);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sp[j][k] = 0x3F803F80u;
-    }
-  }
-  const float beta0 = (a4 & 1) ? -1.0f : 1.0f;
-  const float beta1 = (a4 & 2) ? -1.0f : 1.0f;
-  const float beta2 = (a4 & 4) ? -1.0f : 1.0f;
-  const float beta3 = (a4 & 8) ? -1.0f : 1.0f;
-  const float tau = (__builtin_popcount(a4) & 1) ? -1.0f : 1.0f;
-
-  // bf16 rows are software-pipelined: the next row's 4 loads are in flight
-  // while the current row is transformed.
   u32x4 nxt[4];
-  if (IN_BF16 && wave < rows) {
-    const u32x4* xr = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xin) + wave * N);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) nxt[j] = __builtin_nontemporal_load(xr + j * 64 + lg);
-  }
+  if (IN_BF16 && wave < rows) load2048_bf16(L, static_cast<const uint16_t*>(xin) + wave * N, nxt);
 
   for (int64_t row = wave; row < rows; row += nwaves) {
     float v[4][8];
@@ -209,199 +45,116 @@ __global__ __launch_bounds__(256) void rht2048_kernel(const void* __restrict__ x
       u32x4 raw[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) raw[j] = nxt[j];
-      if (row + nwaves < rows) {
-        const u32x4* xn =
-            reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(xin) + (row + nwaves) * N);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) nxt[j] = __builtin_nontemporal_load(xn + j * 64 + lg);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-        // element bits 0 and 1: the 4-point Hadamard of (d*x)[4h .. 4h+3]
-        // from the two packed bf16 pairs, six dot products
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t p0 = w[2 * h], p1 = w[2 * h + 1];
-          const uint32_t s0 = sp[j][2 * h], s1 = sp[j][2 * h + 1];
-          const float A = dot2_pp(p0, s0);           // u0 + u1
-          const float B = dot2_pm(p0, s0);           // u0 - u1
-          v[j][4 * h + 0] = dot2_pp_c(p1, s1, A);    // u0 + u1 + u2 + u3
-          v[j][4 * h + 1] = dot2_pm_c(p1, s1, B);    // u0 - u1 + u2 - u3
-          v[j][4 * h + 2] = dot2_mm_c(p1, s1, A);    // u0 + u1 - u2 - u3
-          v[j][4 * h + 3] = dot2_mp_c(p1, s1, B);    // u0 - u1 - u2 + u3
-        }
-      }
+      if (row + nwaves < rows)
+        load2048_bf16(L, static_cast<const uint16_t*>(xin) + (row + nwaves) * N, nxt);
+      fwht2048_first_bf16(L, raw, v);
     } else {
-      const f32x4* xr = reinterpret_cast<const f32x4*>(static_cast<const float*>(xin) + row * N);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 a = __builtin_nontemporal_load(xr + j * 128 + 2 * lg);
-        const f32x4 b = __builtin_nontemporal_load(xr + j * 128 + 2 * lg + 1);
-        const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float d0 = (sp[j][k] & 0x8000u) ? -1.0f : 1.0f;
-          const float d1 = (sp[j][k] & 0x80000000u) ? -1.0f : 1.0f;
-          const float u0 = f[2 * k] * d0;
-          v[j][2 * k] = fmaf(f[2 * k + 1], d1, u0);
-          v[j][2 * k + 1] = fmaf(f[2 * k + 1], -d1, u0);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 4) {
-          bfly(v[j][e], v[j][e + 2]);
-          bfly(v[j][e + 1], v[j][e + 3]);
-        }
-      }
+      fwht2048_first_f32(L, static_cast<const float*>(xin) + row * N, v);
     }
-    // element bit 2 (registers e)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bfly(v[j][e], v[j][e + 4]);
-    // element bits 9, 10 (registers j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      bfly(v[0][e], v[1][e]);
-      bfly(v[2][e], v[3][e]);
-      bfly(v[0][e], v[2][e]);
-      bfly(v[1][e], v[3][e]);
-    }
-    // element bit 8: lane bit 5 <-> register bit j1, then butterfly
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j][e]),
-                                                        __float_as_uint(v[j + 2][e]), false, false);
-        v[j][e] = __uint_as_float(r[0]);
-        v[j + 2][e] = __uint_as_float(r[1]);
-        bfly(v[j][e], v[j + 2][e]);
-      }
-    // element bit 7: lane bit 4 <-> register bit j0, then butterfly
-#pragma unroll
-    for (int j = 0; j < 4; j += 2)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j][e]),
-                                                        __float_as_uint(v[j + 1][e]), false, false);
-        v[j][e] = __uint_as_float(r[0]);
-        v[j + 1][e] = __uint_as_float(r[1]);
-        bfly(v[j][e], v[j + 1][e]);
-      }
-    // element bits 3-6 (lane bits 0-3), logical bits 0, 1, 3, 2 via DPP
-    {
-      float* lo = &v[0][0];   // registers of j = 0, 1
-      float* hi = &v[2][0];   // registers of j = 2, 3
-      HR_FMAC_DPP16(lo, beta0, "quad_perm:[1,0,3,2]");
-      HR_FMAC_DPP16(hi, beta0, "quad_perm:[1,0,3,2]");
-      HR_FMAC_DPP16(lo, beta1, "quad_perm:[2,3,0,1]");
-      HR_FMAC_DPP16(hi, beta1, "quad_perm:[2,3,0,1]");
-      HR_FMAC_DPP16(lo, beta3, "row_ror:8");
-      HR_FMAC_DPP16(hi, beta3, "row_ror:8");
-      HR_FMAC_DPP16(lo, beta2, "row_half_mirror");
-      HR_FMAC_DPP16(hi, beta2, "row_half_mirror");
-    }
-
-    // lane l, register (j, e) now holds tau times element
-    //   e | a4 << 3 | (j & 1) << 7 | (j >> 1) << 8 | (l >> 4) << 9
-    const int ebase0 = a4 * 8 + (lane >> 4) * 512;
-    const float ntau = norm * tau;
-
+    fwht2048_rest(L, v);
     if (OUT_F32) {
-      float* yr = yout + row * N;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int base = ebase0 + (j & 1) * 128 + (j >> 1) * 256;
-        f32x4* dst = reinterpret_cast<f32x4*>(yr + base);
-        const f32x4 o0 = {v[j][0] * ntau, v[j][1] * ntau, v[j][2] * ntau, v[j][3] * ntau};
-        const f32x4 o1 = {v[j][4] * ntau, v[j][5] * ntau, v[j][6] * ntau, v[j][7] * ntau};
-        __builtin_nontemporal_store(o0, dst);
-        __builtin_nontemporal_store(o1, dst + 1);
-      }
+      store2048_f32(L, v, norm * L.tau, yout + row * N);
     } else {
-      // ---- group absmax of the unnormalised values
-      float m[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float a = fmaxf(fabsf(v[j][0]), fabsf(v[j][1]));
-#pragma unroll
-        for (int e = 2; e < 8; ++e) a = fmaxf(a, fabsf(v[j][e]));
-        uint32_t ab = __float_as_uint(a);
-        ab = umax_dpp<kQuadXor1>(ab);
-        ab = umax_dpp<kQuadXor2>(ab);
-        if (G >= 64) ab = umax_dpp<kRowHalfMirror>(ab);
-        if (G >= 128) ab = umax_dpp<kRowMirror>(ab);
-        m[j] = __uint_as_float(ab);
-      }
-      if (G == 256) {
-        m[0] = m[1] = fmaxf(m[0], m[1]);
-        m[2] = m[3] = fmaxf(m[2], m[3]);
-      }
-      // ---- scale of one group per lane: lane computes the group of register
-      // block js (G <= 128: js = lane & 3; G = 256: js = 2 * (lane & 1))
-      const int js = (G == 256) ? 2 * (lane & 1) : (lane & 3);
-      const float mv = js == 0 ? m[0] : js == 1 ? m[1] : js == 2 ? m[2] : m[3];
-      const float a = mv * norm;                 // absmax of y = v * norm (norm > 0)
-      const float s32 = div7(a);
-      float s;
-      if (SCALE_F16) s = (float)(_Float16)s32; else s = s32;
-      float k = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s) : 0.0f;
-      // fp16-subnormal (or fp32-denormal) scales are imprecise: clamp needed
-      const bool need_clamp = s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
-      // writer lanes store the scale of their group
-      {
-        int g = -1;
-        if (G == 32) g = (a4 >> 2) + 4 * js + 16 * (lane >> 4);
-        else if (G == 64) g = (lane & 4) ? -1 : (a4 >> 3) + 2 * js + 8 * (lane >> 4);
-        else if (G == 128) g = (lane & 12) ? -1 : js + 4 * (lane >> 4);
-        else g = (lane & 14) ? -1 : (js >> 1) + 2 * (lane >> 4);
-        if (g >= 0) {
-          const int64_t si = row * (N / (G > 0 ? G : 1)) + g;
-          if (SCALE_F16) reinterpret_cast<_Float16*>(scales)[si] = (_Float16)s32;
-          else reinterpret_cast<float*>(scales)[si] = s32;
-        }
-      }
-      // broadcast each group's multiplier to every lane of its quad
-      float kj[4];
-      if (G == 256) {
-        kj[0] = kj[1] = qbcast<0x00>(k);          // quad_perm [0,0,0,0]
-        kj[2] = kj[3] = qbcast<0x55>(k);          // quad_perm [1,1,1,1]
-      } else {
-        kj[0] = qbcast<0x00>(k);
-        kj[1] = qbcast<0x55>(k);
-        kj[2] = qbcast<0xAA>(k);
-        kj[3] = qbcast<0xFF>(k);
-      }
-      // the lane sign tau is this lane's own, so it is applied after the broadcast
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kj[j] *= tau;
-      const bool clamp = __builtin_amdgcn_ballot_w64(need_clamp) != 0;
-      const float M = 12582920.0f;              // 1.5 * 2^23 + 8
-      uint32_t* cr = reinterpret_cast<uint32_t*>(codes + row * (N / 2));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float r[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = fmaf(v[j][e], kj[j], M);
-        if (clamp) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] = __builtin_amdgcn_fmed3f(r[e], M - 7.0f, M + 7.0f);
-        }
-        const int dw = a4 + (j & 1) * 16 + (j >> 1) * 32 + (lane >> 4) * 64;
-        __builtin_nontemporal_store(pack8(r), cr + dw);
-      }
+      quant2048<G, SCALE_F16>(L, v, norm, L.tau,
+                              reinterpret_cast<uint32_t*>(codes + row * (N / 2)), scales,
+                              row * (N / (G > 0 ? G : 1)));
     }
   }
 }
 
 template <bool IN_BF16, int G, bool SCALE_F16, bool OUT_F32>
+__global__ __launch_bounds__(1024) void mixed2048_kernel(const void* __restrict__ xin,
+                                                          const int8_t* __restrict__ signs,
+                                                          const float* __restrict__ block, int m,
+                                                          int64_t rows, float* __restrict__ yout,
+                                                          uint8_t* __restrict__ codes,
+                                                          void* __restrict__ scales, float norm) {
+  constexpr int P = 2048;
+  extern __shared__ f32x4 lds4[];               // m chunks x 2048 floats
+  float* lds = reinterpret_cast<float*>(lds4);
+  const int w = threadIdx.x >> 6;               // chunk of this wave
+  const int64_t n = (int64_t)m * P;
+  Lane2048 L;
+  lane2048_init(L, signs ? signs + (int64_t)w * P : nullptr);
+  float o[16];                                  // row w of the orthogonal block
+#pragma unroll
+  for (int c = 0; c < 16; ++c) o[c] = c < m ? block[w * m + c] : 0.0f;
+
+  u32x4 nxt[4];
+  if (IN_BF16 && (int64_t)blockIdx.x < rows)
+    load2048_bf16(L, static_cast<const uint16_t*>(xin) + (int64_t)blockIdx.x * n + (int64_t)w * P, nxt);
+
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    float v[4][8];
+    if (IN_BF16) {
+      u32x4 raw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) raw[j] = nxt[j];
+      if (row + gridDim.x < rows)
+        load2048_bf16(L, static_cast<const uint16_t*>(xin) + (row + gridDim.x) * n + (int64_t)w * P, nxt);
+      fwht2048_first_bf16(L, raw, v);
+    } else {
+      fwht2048_first_f32(L, static_cast<const float*>(xin) + row * n + (int64_t)w * P, v);
+    }
+    fwht2048_rest(L, v);
+    // chunk w (true values) to LDS in natural element order
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4* dst = reinterpret_cast<f32x4*>(lds + w * P + elem2048(L, j));
+      dst[0] = (f32x4){v[j][0] * L.tau, v[j][1] * L.tau, v[j][2] * L.tau, v[j][3] * L.tau};
+      dst[1] = (f32x4){v[j][4] * L.tau, v[j][5] * L.tau, v[j][6] * L.tau, v[j][7] * L.tau};
+    }
+    __syncthreads();
+    // output chunk w at the same positions: sum_c O[w][c] * chunk_c
+    float acc[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
+    for (int c = 0; c < m; ++c) {
+      const float oc = o[c];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(lds + c * P + elem2048(L, j));
+        const f32x4 p0 = src[0], p1 = src[1];
+        acc[j][0] = fmaf(oc, p0.x, acc[j][0]);
+        acc[j][1] = fmaf(oc, p0.y, acc[j][1]);
+        acc[j][2] = fmaf(oc, p0.z, acc[j][2]);
+        acc[j][3] = fmaf(oc, p0.w, acc[j][3]);
+        acc[j][4] = fmaf(oc, p1.x, acc[j][4]);
+        acc[j][5] = fmaf(oc, p1.y, acc[j][5]);
+        acc[j][6] = fmaf(oc, p1.z, acc[j][6]);
+        acc[j][7] = fmaf(oc, p1.w, acc[j][7]);
+      }
+    }
+    if (OUT_F32) {
+      store2048_f32(L, acc, norm, yout + row * n + (int64_t)w * P);
+    } else {
+      quant2048<G, SCALE_F16>(L, acc, norm, 1.0f,
+                              reinterpret_cast<uint32_t*>(codes + row * (n / 2) + (int64_t)w * (P / 2)),
+                              scales, row * (n / (G > 0 ? G : 1)) + (int64_t)w * (P / (G > 0 ? G : 1)));
+    }
+    __syncthreads();                            // LDS is rewritten by the next row
+  }
+}
+
+template <bool IN_BF16, int G, bool SCALE_F16, bool OUT_F32>
 static void launch_one(const RhtArgs& a, float norm, hipStream_t s) {
-  int64_t blocks = (a.rows + 3) / 4;   // one wave per row, 4 waves per block
-  const int64_t cap = 256 * HR_RHT2048_BLOCKS_PER_CU;
-  if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((rht2048_kernel<IN_BF16, G, SCALE_F16, OUT_F32>), dim3((unsigned)blocks),
-                     dim3(256), 0, s, a.x, a.signs, a.rows, a.y, a.codes, a.scales, norm);
+  if (a.m == 1) {
+    int64_t blocks = (a.rows + 3) / 4;   // one wave per row, 4 waves per block
+    const int64_t cap = 256 * HR_RHT2048_BLOCKS_PER_CU;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL((rht2048_kernel<IN_BF16, G, SCALE_F16, OUT_F32>), dim3((unsigned)blocks),
+                       dim3(256), 0, s, a.x, a.signs, a.rows, a.y, a.codes, a.scales, norm);
+  } else {
+    // one row per workgroup of m waves; LDS holds the row (m * 8 KB)
+    const size_t lds = (size_t)a.m * 2048 * sizeof(float);
+    const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+    const int64_t blocks = a.rows < 256 * per_cu ? a.rows : 256 * per_cu;
+    hipLaunchKernelGGL((mixed2048_kernel<IN_BF16, G, SCALE_F16, OUT_F32>), dim3((unsigned)blocks),
+                       dim3(64 * a.m), lds, s, a.x, a.signs, a.block, a.m, a.rows, a.y, a.codes,
+                       a.scales, norm);
+  }
 }
 
 template <bool IN_BF16>
@@ -426,10 +179,11 @@ static bool dispatch_in(const RhtArgs& a, float norm, hipStream_t s) {
 #undef HR_Q
 }
 
-// Handles n == 2048, m == 1 (fp32 output or fused quantization).  Returns
-// false when the case belongs to the general kernel.
+// Handles p == 2048 (n = m * 2048, 1 <= m <= 16), fp32 output or fused
+// quantization.  Returns false when the case belongs to the general kernel.
 bool launch_rht2048(const RhtArgs& a, hipStream_t s) {
-  if (a.n != 2048 || a.m != 1) return false;
+  if (a.p != 2048 || a.m < 1 || a.m > 16) return false;
+  if (a.m > 1 && (size_t)a.m * 2048 * sizeof(float) > 160 * 1024) return false;
   const float norm = (float)(1.0 / sqrt(2048.0));
   return a.x_bf16 ? dispatch_in<true>(a, norm, s) : dispatch_in<false>(a, norm, s);
 }

@@ -112,7 +112,8 @@ def test_rotate_quant_large_dynamic_range():
 
 # ---------------------------------------------------------------- mixed radix
 
-@pytest.mark.parametrize("m,p,group", [(7, 2048, 128), (3, 64, 32), (5, 256, 64), (16, 1024, 128)])
+@pytest.mark.parametrize("m,p,group", [(7, 2048, 128), (3, 64, 32), (5, 256, 64), (16, 1024, 128),
+                                       (2, 2048, 32), (3, 2048, 256), (8, 2048, 64)])
 def test_mixed_radix(m, p, group):
     hr = _hr()
     rows = 23
@@ -125,6 +126,20 @@ def test_mixed_radix(m, p, group):
     check_rotated(y, y64)
     codes, scales = hr.rotate_quant_int4(xd, group, dd, od)
     check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, "f16")
+
+
+def test_mixed_radix_fp32_input_fp32_scales():
+    hr = _hr()
+    m, p, group = 5, 2048, 128
+    mi = hr_inputs.mixed_inputs(rows=17, m=m, p=p, seed=333)
+    x = mi.x.float()
+    xd = x.to(DEV)
+    dd = torch.from_numpy(mi.signs).to(DEV)
+    od = torch.from_numpy(mi.block).to(DEV)
+    y64 = oracle.mixed_radix.mixed_radix(x.numpy(), mi.signs, mi.block, p)
+    check_rotated(hr.rotate(xd, dd, od).cpu().numpy(), y64)
+    codes, scales = hr.rotate_quant_int4(xd, group, dd, od, scale_dtype=torch.float32)
+    check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, "f32")
 
 
 # ---------------------------------------------------------------- butterfly
