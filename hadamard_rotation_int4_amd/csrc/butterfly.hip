@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kBfThreads) void butterfly_generic_kernel(Butterfly
 }
 
 hipError_t launch_butterfly(const ButterflyArgs& a, hipStream_t s) {
+  if (launch_butterfly4096(a, s)) return hipGetLastError();
   const int64_t grid64 = a.rows < 4096 ? a.rows : 4096;
   const dim3 grid((unsigned)grid64), block(kBfThreads);
   const size_t lds = 2 * sizeof(float) * (size_t)a.n;

@@ -1,0 +1,238 @@
+// HARP-style butterfly for n = 4096: 12 stages of 2x2 blocks on pairs at
+// stride 2^s, then the gather permutation; optional fused int4 quantization.
+//
+// Source: HARP abstract (a rotation as a product of sparse butterfly-like
+// block-orthogonal stages) and HARP technical summary (gist.science), sections
+// 2.1 (stride stages), 2.2 (block kernel Q(theta) G_2) and 2.4 (O(d log d)
+// application without materialised permutations).
+//
+// One workgroup of 512 threads per row, persistent over rows.  Each thread
+// owns 8 elements of the row per pass; the 12 stages run as 4 passes of 3
+// register stages.  In pass k the thread's 8 registers are the elements whose
+// index bits 3k..3k+2 take all 8 values, the other 9 bits being the thread
+// index; between passes the row goes through LDS.  Because a thread owns the
+// same pairs in every row, its 12 x 4 pairs' coefficients stay in registers
+// for the kernel's lifetime.  The LDS index is padded by 8 floats every 64
+// (p = i + 8 * (i >> 6)) so that the one strided pass (k = 1) is bank-conflict
+// free; the other passes access consecutive elements.
+#include "hr_internal.h"
+#include "fwht2048.h"
+
+namespace hr {
+
+constexpr int kBfN = 4096;
+constexpr int kBfThreads4096 = 512;
+constexpr int kBfLds = kBfN + 8 * (kBfN / 64);
+
+__device__ __forceinline__ int bf_pad(int i) { return i + 8 * (i >> 6); }
+
+// element index of register r of thread t in pass k: bits 3k..3k+2 = r
+__device__ __forceinline__ int bf_idx(int t, int k, int r) {
+  const int lo = t & ((1 << (3 * k)) - 1);
+  const int hi = t >> (3 * k);
+  return lo | (r << (3 * k)) | (hi << (3 * k + 3));
+}
+
+// register holding the lower element of pair q (0..3) of the stage on
+// register bit b
+__device__ __forceinline__ constexpr int bf_r0(int q, int b) {
+  return ((q >> b) << (b + 1)) | (q & ((1 << b) - 1));
+}
+
+template <bool PRECOND, bool TRANSPOSE>
+__device__ __forceinline__ void bf_block(float& a, float& b, float2 k) {
+  const float u = a, v = b;
+  if (PRECOND) {                 // [[k.x, k.y], [k.y, -k.x]] (symmetric)
+    a = fmaf(k.x, u, k.y * v);
+    b = fmaf(k.y, u, -k.x * v);
+  } else if (!TRANSPOSE) {       // [[c, -s], [s, c]]
+    a = fmaf(k.x, u, -k.y * v);
+    b = fmaf(k.y, u, k.x * v);
+  } else {                       // [[c, s], [-s, c]]
+    a = fmaf(k.x, u, k.y * v);
+    b = fmaf(-k.y, u, k.x * v);
+  }
+}
+
+template <bool PRECOND, bool TRANSPOSE>
+__device__ __forceinline__ void bf_stage(float (&v)[8], const float2 (&cf)[4], int b) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r0 = bf_r0(q, b);
+    bf_block<PRECOND, TRANSPOSE>(v[r0], v[r0 | (1 << b)], cf[q]);
+  }
+}
+
+template <bool PRECOND, bool INVERSE, bool OUT_Y, int G, bool SCALE_F16>
+__global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
+    const float* __restrict__ x, float* __restrict__ y, int64_t rows,
+    const float2* __restrict__ coeffs, const int* __restrict__ perm,
+    uint8_t* __restrict__ codes, void* __restrict__ scales) {
+  constexpr int N = kBfN, HALF = N / 2;
+  __shared__ __attribute__((aligned(16))) float lds[2][kBfLds];
+  const int t = threadIdx.x;
+
+  // per-thread coefficients of its 4 pairs in each of the 12 stages
+  float2 cf[12][4];
+#pragma unroll
+  for (int s = 0; s < 12; ++s) {
+    const int k = s / 3, b = s % 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = bf_idx(t, k, bf_r0(q, b));
+      const int p = ((i >> (s + 1)) << s) | (i & ((1 << s) - 1));
+      cf[s][q] = coeffs[s * HALF + p];
+    }
+  }
+  int pm[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) pm[r] = perm ? perm[8 * t + r] : 8 * t + r;
+
+  // the next row's 8 elements are in flight while the current row is processed
+  f32x4 n0, n1;
+  if ((int64_t)blockIdx.x < rows) {
+    const f32x4* xr = reinterpret_cast<const f32x4*>(x + (int64_t)blockIdx.x * N) + 2 * t;
+    n0 = __builtin_nontemporal_load(xr);
+    n1 = __builtin_nontemporal_load(xr + 1);
+  }
+
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    float v[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+    if (row + gridDim.x < rows) {
+      const f32x4* xr = reinterpret_cast<const f32x4*>(x + (row + gridDim.x) * N) + 2 * t;
+      n0 = __builtin_nontemporal_load(xr);
+      n1 = __builtin_nontemporal_load(xr + 1);
+    }
+    if (!INVERSE) {
+      // pass 0: stages 0, 1, 2 on elements 8t .. 8t+7
+#pragma unroll
+      for (int b = 0; b < 3; ++b) bf_stage<PRECOND, false>(v, cf[b], b);
+      int buf = 0;
+#pragma unroll
+      for (int k = 1; k < 4; ++k) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, k - 1, r))] = v[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, k, r))];
+#pragma unroll
+        for (int b = 0; b < 3; ++b) bf_stage<PRECOND, false>(v, cf[3 * k + b], b);
+        buf ^= 1;
+      }
+      // gather: out[8t + r] = z[perm[8t + r]]
+#pragma unroll
+      for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, 3, r))] = v[r];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(pm[r])];
+    } else {
+      // scatter z[perm[i]] = x[i], then the transposed stages in reverse order
+#pragma unroll
+      for (int r = 0; r < 8; ++r) lds[0][bf_pad(pm[r])] = v[r];
+      __syncthreads();
+      int buf = 0;
+#pragma unroll
+      for (int k = 3; k >= 1; --k) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, k, r))];
+#pragma unroll
+        for (int b = 2; b >= 0; --b) bf_stage<PRECOND, true>(v, cf[3 * k + b], b);
+        buf ^= 1;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, k, r))] = v[r];
+        __syncthreads();
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, 0, r))];
+#pragma unroll
+      for (int b = 2; b >= 0; --b) bf_stage<PRECOND, true>(v, cf[b], b);
+    }
+    // thread t now holds output elements 8t .. 8t+7
+    if (OUT_Y) {
+      f32x4* yr = reinterpret_cast<f32x4*>(y + row * N) + 2 * t;
+      __builtin_nontemporal_store((f32x4){v[0], v[1], v[2], v[3]}, yr);
+      __builtin_nontemporal_store((f32x4){v[4], v[5], v[6], v[7]}, yr + 1);
+    }
+    if (G > 0) {
+      // group of G = G/8 consecutive lanes x 8 registers
+      float a = fmaxf(fabsf(v[0]), fabsf(v[1]));
+#pragma unroll
+      for (int r = 2; r < 8; ++r) a = fmaxf(a, fabsf(v[r]));
+      uint32_t ab = __float_as_uint(a);
+      ab = umax_dpp<kQuadXor1>(ab);
+      ab = umax_dpp<kQuadXor2>(ab);
+      if (G >= 64) ab = umax_dpp<kRowHalfMirror>(ab);
+      if (G >= 128) ab = umax_dpp<kRowMirror>(ab);
+      if (G >= 256) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)ab, 16, 64);
+        ab = ab > o ? ab : o;
+      }
+      const float s32 = div7(__uint_as_float(ab));
+      const float s = SCALE_F16 ? (float)(_Float16)s32 : s32;
+      float k = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+      const bool need_clamp = s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
+      const bool clamp = __builtin_amdgcn_ballot_w64(need_clamp) != 0;
+      const float M = 12582920.0f;              // 1.5 * 2^23 + 8
+      float r8[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) r8[r] = fmaf(v[r], k, M);
+      if (clamp) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) r8[r] = __builtin_amdgcn_fmed3f(r8[r], M - 7.0f, M + 7.0f);
+      }
+      __builtin_nontemporal_store(pack8(r8), reinterpret_cast<uint32_t*>(codes + row * (N / 2)) + t);
+      if ((t & (G / 8 - 1)) == 0) {
+        const int64_t si = row * (N / G) + (8 * t) / G;
+        if (SCALE_F16) reinterpret_cast<_Float16*>(scales)[si] = (_Float16)s32;
+        else reinterpret_cast<float*>(scales)[si] = s32;
+      }
+    }
+  }
+}
+
+template <bool PRECOND, bool INVERSE, bool OUT_Y, int G, bool F16>
+static void bf_launch(const ButterflyArgs& a, hipStream_t s) {
+  const int64_t blocks = a.rows < 256 ? a.rows : 256;
+  hipLaunchKernelGGL((butterfly4096_kernel<PRECOND, INVERSE, OUT_Y, G, F16>), dim3((unsigned)blocks),
+                     dim3(kBfThreads4096), 0, s, a.x, a.y, a.rows,
+                     reinterpret_cast<const float2*>(a.coeffs), a.perm, a.codes, a.scales);
+}
+
+template <bool PRECOND>
+static bool bf_dispatch(const ButterflyArgs& a, hipStream_t s) {
+  if (a.inverse) {
+    if (a.codes || !a.y) return false;
+    bf_launch<PRECOND, true, true, 0, false>(a, s);
+    return true;
+  }
+  if (!a.codes) {
+    bf_launch<PRECOND, false, true, 0, false>(a, s);
+    return true;
+  }
+#define HR_BFQ(G)                                                                     \
+  case G:                                                                             \
+    if (a.y) {                                                                        \
+      if (a.scale_f16) bf_launch<PRECOND, false, true, G, true>(a, s);                \
+      else bf_launch<PRECOND, false, true, G, false>(a, s);                           \
+    } else {                                                                          \
+      if (a.scale_f16) bf_launch<PRECOND, false, false, G, true>(a, s);               \
+      else bf_launch<PRECOND, false, false, G, false>(a, s);                          \
+    }                                                                                 \
+    return true;
+  switch (a.group) {
+    HR_BFQ(32)
+    HR_BFQ(64)
+    HR_BFQ(128)
+    HR_BFQ(256)
+    default: return false;
+  }
+#undef HR_BFQ
+}
+
+// Handles n == 4096; returns false for other sizes (general kernel).
+bool launch_butterfly4096(const ButterflyArgs& a, hipStream_t s) {
+  if (a.n != kBfN) return false;
+  return a.precondition ? bf_dispatch<true>(a, s) : bf_dispatch<false>(a, s);
+}
+
+}  // namespace hr

@@ -54,6 +54,7 @@ bool launch_rht2048(const RhtArgs& a, hipStream_t s);  // false: not handled
 hipError_t launch_butterfly_coeffs(const float* angles, int n, int log2n, int precondition,
                                    float* coeffs, hipStream_t s);
 hipError_t launch_butterfly(const ButterflyArgs& a, hipStream_t s);
+bool launch_butterfly4096(const ButterflyArgs& a, hipStream_t s);  // false: not handled
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int scale_f16, int64_t rows,
                           int n, int group, float* out, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
