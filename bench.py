@@ -12,6 +12,9 @@ Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +27,36 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA peak
 METRIC = "fused RHT+int4 quant GB/s (% of HBM peak) at K=2048; W4A4 GEMM int8 TOPS"
 
 ROWS, N, GROUP = 65536, 2048, 128
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(HERE, "profiles")
+CSRC = os.path.join(HERE, "hadamard_rotation_int4_amd", "csrc")
+# sources that make up the headline kernel (its counters go stale when they change)
+MAIN_KERNEL_SOURCES = ("rht2048.hip", "fwht2048.h", "hr_device.h", "hr_internal.h")
+MAIN_KERNEL_NAME = "rht2048_kernel<true, 128, true, false>"
+TRAFFIC_FILE = os.path.join(PROFILES, "rht_quant_bf16_65536x2048_g128.traffic.json")
+COPY_BYTES = 512 * 1024 * 1024       # calibration copy: reads and writes this many bytes
+
+
+def main_kernel_hash():
+    h = hashlib.sha256()
+    for name in MAIN_KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter
+    summary, or None when it is missing or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != main_kernel_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
 
 
 def rht_alg_bytes(rows, n, group, in_bytes=2, scale_bytes=2):
@@ -88,7 +121,13 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time only the headline kernel")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="run the headline kernel and a plain copy (for rocprofv3 --pmc), print nothing")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="turn rocprofv3 outputs under DIR (ktrace/, fetch/, write/) into profiles/")
     args = ap.parse_args(argv)
+    if args.summarize_profile:
+        return summarize_profile(args.summarize_profile)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU only (rows are independent; see DESIGN.md "
               "for how it would shard); run with --gpus 1", file=sys.stderr)
@@ -112,6 +151,16 @@ def main(argv=None):
 
     def step(i):
         hr.rotate_quant_int4(xs[i], GROUP, d, codes=codes[i], scales=scales[i])
+
+    if args.profile_run:
+        for i in range(args.steps):
+            step(i % nbuf)
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)         # plain elementwise pass: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        return 0
 
     ms = _timed(step, args.steps, args.warmup, nbuf)
     alg = rht_alg_bytes(ROWS, N, GROUP)
@@ -209,7 +258,8 @@ def main(argv=None):
                                "G=128, seeded signs, 0.1% outlier channels x50",
                    "rows": ROWS, "n": N, "group": GROUP},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic()},
     }
     g4096 = kernels.get("w4a4_gemm_4096x4096x4096_g128")
     if g4096:
@@ -220,6 +270,70 @@ def main(argv=None):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def _read_csv(pattern):
+    rows = []
+    for path in glob.glob(pattern, recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _counter_per_dispatch(rows, kernel_substr, counter):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def summarize_profile(d):
+    """Write the kernel-duration summary and the HBM-traffic summary of the
+    headline kernel from rocprofv3 outputs under d/ktrace, d/fetch, d/write."""
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = _read_csv(os.path.join(d, "ktrace", "**", "*kernel_stats.csv"))
+    lines = ["# rocprofv3 --kernel-trace --stats summary (times in microseconds)",
+             "# command: rocprofv3 --kernel-trace --stats -d <dir>/ktrace -o run -- "
+             "python bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+             "kernel | calls | avg_us | min_us | max_us | total_%"]
+    for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+        lines.append(" | ".join([r["Name"][:110], r["Calls"],
+                                 f"{float(r['AverageNs']) / 1e3:.2f}", f"{float(r['MinNs']) / 1e3:.2f}",
+                                 f"{float(r['MaxNs']) / 1e3:.2f}", f"{float(r['Percentage']):.2f}"]))
+    with open(os.path.join(PROFILES, "kernel_stats_bench_default.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    fetch = _read_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
+    write = _read_csv(os.path.join(d, "write", "**", "*counter_collection.csv"))
+    kf, nk = _counter_per_dispatch(fetch, "rht2048_kernel", "FETCH_SIZE")
+    kw, _ = _counter_per_dispatch(write, "rht2048_kernel", "WRITE_SIZE")
+    cf = cw = None
+    nc = 0
+    copy_kernel = None
+    for pat in ("neg_kernel",):           # the elementwise negation of COPY_BYTES
+        cf, nc = _counter_per_dispatch(fetch, pat, "FETCH_SIZE")
+        cw, _ = _counter_per_dispatch(write, pat, "WRITE_SIZE")
+        if cf and cw:
+            copy_kernel = pat
+            break
+    out = {"kernel": MAIN_KERNEL_NAME, "workload": "bf16 65536x2048, G=128, fp16 scales",
+           "source_hash": main_kernel_hash(),
+           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir>/fetch -o run -- "
+                      "python bench.py --profile-run --steps 20",
+           "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": nk,
+           "copy_kernel_match": copy_kernel, "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf,
+           "copy_write_kib": cw, "copy_dispatches": nc}
+    if None not in (kf, kw, cf, cw):
+        ff = COPY_BYTES / (cf * 1024.0)
+        fw = COPY_BYTES / (cw * 1024.0)
+        out.update({"fetch_scale": ff, "write_scale": fw,
+                    "fetch_bytes_per_launch": kf * 1024.0 * ff,
+                    "write_bytes_per_launch": kw * 1024.0 * fw,
+                    "traffic_bytes_per_launch": kf * 1024.0 * ff + kw * 1024.0 * fw,
+                    "algorithmic_bytes_per_launch": rht_alg_bytes(ROWS, N, GROUP)})
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
     return 0
 
 
