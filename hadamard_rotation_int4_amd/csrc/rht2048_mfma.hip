@@ -1,0 +1,316 @@
+// Randomized Hadamard transform of bf16 rows of 2048 elements, fused with
+// int4 quantization (or an fp32 store), with the 128-point factor of the
+// transform on bf16 matrix cores.
+//
+// What is computed: y = H_2048 (d * x) / sqrt(2048) per row, Sylvester order
+// ("Experiment -- Hadamard rotation for int4 (W4A4) accuracy", Hypothesis and
+// Method; "Llama-3.2-1B-Instruct-HadamardSpin-4bits", How it Works), then
+// groups of G consecutive outputs quantized with scale absmax / 7 (same
+// pages, Method).
+//
+// Factorisation.  Write an element index as 128 a + k (a < 16, k < 128).
+// H_2048[128a + k][128a' + c] = H_16[a][a'] H_128[k][c], so
+//   Z[a][c]  = sum_k H_128[c][k] u[a][k]      u = d * x (exact in bf16)
+//   Y[a'][c] = sum_a H_16[a'][a] Z[a][c]
+// The first is a 128 x 128 contraction with +-1 entries and bf16 data; it runs
+// on v_mfma_f32_16x16x32_bf16 with fp32 accumulation (every product is
+// exact).  The second is four butterfly stages across the 16 lanes of a DPP
+// row, as in the register kernel of fwht2048.h (GF(2) lane relabel, per-lane
+// sign tau folded into the output multiplier).
+//
+// Placement (one wave, one row per iteration).  Lane l = q + 16 g:
+//   B operand (data): for K-step s < 4, lane l holds the 8 elements
+//     k = 8 g + 32 s + e (e < 8) of chunk a = A(q), A the GF(2) relabel of
+//     the 16 lanes of a DPP row.
+//   D (tile T < 8): lane l register v holds Z[A(q)][c] for
+//     c = v + 4 T0 + 8 g + 32 T1 + 64 T2 (tile row i = 4 g + v).
+//   A operand (H_128): lane l holds tile row i = q and K group g.  With k bits
+//     (e0 e1 e2 g0 g1 s0 s1) and c bits (i0 i1 T0 i2 i3 T1 T2), the entry is
+//     (-1)^(i0 e0 + i1 e1 + i2 g0 + i3 g1) (-1)^(T0 e2) (-1)^(T1 s0 + T2 s1):
+//     four distinct fragments cover all 32 (T, s) pairs.
+//   Staging: each wave streams its rows through two 4 KB LDS stages filled by
+//     global_load_lds_dwordx4 (two rows in flight per wave without holding
+//     registers).  Load j < 4, lane i fetches the 16-byte piece (chunk i & 15,
+//     piece 4 j + (i >> 4) of the chunk), so global reads come in 64-byte
+//     runs and the 16 pieces a lane group needs for one MFMA are consecutive
+//     LDS slots (no bank conflicts).
+//   Codes: a lane owns four runs of 8 consecutive outputs; they are staged
+//     through LDS (swizzled, conflict-free) and written as one contiguous
+//     1 KB row per store instruction.
+#include "hr_internal.h"
+#include "fwht2048.h"
+
+namespace hr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// The H_16 stages on the eight accumulator tiles, pinned to v[96:127] so that
+// the MFMA results are transformed in place.  One v_fmac_f32_dpp per register
+// and stage: own + beta * partner (partner through DPP).  The block opens with
+// 24 wait states, more than the longest MFMA-write to VALU-read distance (the
+// compiler does not guard inline asm against that hazard); between stages a
+// register is rewritten 32 instructions before its next DPP read, far beyond
+// the two wait states DPP needs.
+#define HR_F1(r, b, CTRL) "v_fmac_f32_dpp v" #r ", v" #r ", %" #b " " CTRL " row_mask:0xf bank_mask:0xf\n\t"
+#define HR_F4(r0, r1, r2, r3, b, CTRL) \
+  HR_F1(r0, b, CTRL) HR_F1(r1, b, CTRL) HR_F1(r2, b, CTRL) HR_F1(r3, b, CTRL)
+#define HR_STAGE32(b, CTRL)         \
+  HR_F4(96, 97, 98, 99, b, CTRL)     \
+  HR_F4(100, 101, 102, 103, b, CTRL) \
+  HR_F4(104, 105, 106, 107, b, CTRL) \
+  HR_F4(108, 109, 110, 111, b, CTRL) \
+  HR_F4(112, 113, 114, 115, b, CTRL) \
+  HR_F4(116, 117, 118, 119, b, CTRL) \
+  HR_F4(120, 121, 122, 123, b, CTRL) \
+  HR_F4(124, 125, 126, 127, b, CTRL)
+
+// Max over the four lanes q, q + 16, q + 32, q + 48 (same DPP-row position).
+__device__ __forceinline__ float max_over_rows(float m) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+constexpr int kMfmaBlocksPerCu = 4;
+
+template <int G, bool SCALE_F16, bool OUT_F32>
+__global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ signs, int64_t rows,
+    float* __restrict__ yout, uint8_t* __restrict__ codes, void* __restrict__ scales, float norm) {
+  constexpr int N = 2048;
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 15;
+  const int g = lane >> 4;
+  const int a4 = (q & 12) | ((q ^ (q >> 2)) & 1) | ((((q >> 1) ^ (q >> 2)) & 1) << 1);
+  const int wib = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wib;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+
+  // H_128 fragments F[T0][global sign]
+  u32x4 F[2][2];
+  {
+    const int i0 = q & 1, i1 = (q >> 1) & 1, i2 = (q >> 2) & 1, i3 = (q >> 3) & 1;
+    const int pl = (i2 & g) ^ (i3 & (g >> 1));
+#pragma unroll
+    for (int t0 = 0; t0 < 2; ++t0)
+#pragma unroll
+      for (int gs = 0; gs < 2; ++gs) {
+        uint32_t w[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int e = 2 * d + hb;
+            const int par = ((i0 & e) ^ (i1 & (e >> 1)) ^ (t0 & (e >> 2)) ^ pl ^ gs) & 1;
+            word |= (par ? 0xBF80u : 0x3F80u) << (16 * hb);
+          }
+          w[d] = word;
+        }
+        F[t0][gs] = (u32x4){w[0], w[1], w[2], w[3]};
+      }
+  }
+  // sign-flip masks of the lane's B-operand elements (bf16 sign bits)
+  u32x4 sm[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (signs) {
+      const uint2 s8 = *reinterpret_cast<const uint2*>(signs + a4 * 128 + 32 * s + 8 * g);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t src = d < 2 ? s8.x : s8.y;
+        const uint32_t b0 = (src >> (16 * (d & 1))) & 0x80u;
+        const uint32_t b1 = (src >> (16 * (d & 1) + 8)) & 0x80u;
+        w[d] = (b0 << 8) | (b1 << 24);
+      }
+    }
+    sm[s] = (u32x4){w[0], w[1], w[2], w[3]};
+  }
+  const float beta0 = (a4 & 1) ? -1.0f : 1.0f;
+  const float beta1 = (a4 & 2) ? -1.0f : 1.0f;
+  const float beta2 = (a4 & 4) ? -1.0f : 1.0f;
+  const float beta3 = (a4 & 8) ? -1.0f : 1.0f;
+  const float tau = (__builtin_popcount(a4) & 1) ? -1.0f : 1.0f;
+
+  // LDS of this wave: two row stages (256 slots of 16 bytes) and one row of codes
+  __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][2][256];
+  __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][64];
+  // element offset of this lane's piece within a row, per load j: + 32 j
+  const int lane_src = 128 * (lane & 15) + 8 * (lane >> 4);
+  auto issue = [&](int64_t row, int st) {
+    const uint16_t* base = x + row * N + lane_src;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(base + 32 * j, &stage_lds[wib][st][64 * j], 16, 0, 0);
+  };
+  // B operands of one row from stage st: lane (q, g) takes slot 64 s + 16 g +
+  // A(q) for K-step s.  One asm block waits for the stage (at most 4 younger
+  // vector-memory ops, the other stage's loads, may still be pending; loads
+  // complete in order) and for its own results.
+  const uint32_t rd_lane = 16u * (uint32_t)(16 * g + a4);
+  auto read_stage = [&](int st, bool next_pending, u32x4 (&b)[4]) {
+    const uint32_t addr = (uint32_t)(uintptr_t)&stage_lds[wib][st][0] + rd_lane;
+#define HR_DSR4(WAIT)                                                                    \
+    asm volatile(WAIT "\n\t"                                                             \
+                 "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"             \
+                 "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t" \
+                 "s_waitcnt lgkmcnt(0)"                                                  \
+                 : "=v"(b[0]), "=v"(b[1]), "=v"(b[2]), "=v"(b[3])                         \
+                 : "v"(addr)                                                             \
+                 : "memory")
+    if (next_pending) HR_DSR4("s_waitcnt vmcnt(4)");
+    else HR_DSR4("s_waitcnt vmcnt(0)");
+#undef HR_DSR4
+  };
+
+  auto process = [&](int64_t row, const u32x4 (&b)[4]) {
+    f32x4 acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 bb = __builtin_bit_cast(bf16x8, b[s] ^ sm[s]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int gs = (((t >> 1) & s) ^ ((t >> 2) & (s >> 1))) & 1;
+        const bf16x8 aa = __builtin_bit_cast(bf16x8, F[t & 1][gs]);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bb, acc[t], 0, 0, 0);
+      }
+    }
+    // H_16 across the lanes of each DPP row (logical chunk bits 0, 1, 3, 2)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+                 HR_STAGE32(8, "quad_perm:[1,0,3,2]")
+                 HR_STAGE32(9, "quad_perm:[2,3,0,1]")
+                 HR_STAGE32(10, "row_ror:8")
+                 HR_STAGE32(11, "row_half_mirror")
+                 : "+{v[96:99]}"(acc[0]), "+{v[100:103]}"(acc[1]), "+{v[104:107]}"(acc[2]),
+                   "+{v[108:111]}"(acc[3]), "+{v[112:115]}"(acc[4]), "+{v[116:119]}"(acc[5]),
+                   "+{v[120:123]}"(acc[6]), "+{v[124:127]}"(acc[7])
+                 : "v"(beta0), "v"(beta1), "v"(beta3), "v"(beta2));
+    // lane now holds tau * Y[a4][c], c = v + 4 T0 + 8 g + 32 T1 + 64 T2
+    if (OUT_F32) {
+      const float ym = norm * tau;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        f32x4* dst = reinterpret_cast<f32x4*>(yout + row * N + 128 * a4 + 32 * m + 8 * g);
+        const f32x4 lo = acc[2 * m], hi = acc[2 * m + 1];
+        dst[0] = (f32x4){lo[0] * ym, lo[1] * ym, lo[2] * ym, lo[3] * ym};
+        dst[1] = (f32x4){hi[0] * ym, hi[1] * ym, hi[2] * ym, hi[3] * ym};
+      }
+      return;
+    }
+    // group absmax: run m (outputs 32 m + 8 g + 0..7) is tiles 2m, 2m+1
+    float mr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 lo = acc[2 * m], hi = acc[2 * m + 1];
+      mr[m] = fmaxf(fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])), fmaxf(fabsf(lo[2]), fabsf(lo[3]))),
+                    fmaxf(fmaxf(fabsf(hi[0]), fabsf(hi[1])), fmaxf(fabsf(hi[2]), fabsf(hi[3]))));
+    }
+    constexpr int NG = G == 32 ? 4 : G == 64 ? 2 : 1;   // groups per lane (shared by its 4 rows)
+    float mg[NG];
+    if (G == 32) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) mg[m] = mr[m];
+    } else if (G == 64) {
+      mg[0] = fmaxf(mr[0], mr[1]);
+      mg[NG - 1] = fmaxf(mr[2], mr[3]);
+    } else {
+      mg[0] = fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3]));
+    }
+#pragma unroll
+    for (int i = 0; i < NG; ++i) mg[i] = max_over_rows(mg[i]);
+    if (G == 256) mg[0] = __uint_as_float(umax_dpp<kQuadXor1>(__float_as_uint(mg[0])));
+    float kk[NG];
+    float s_own = 0.0f;                  // scale of the group this lane stores
+    bool need_clamp = false;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const float s32 = div7(mg[i] * norm);
+      const float s = SCALE_F16 ? (float)(_Float16)s32 : s32;
+      kk[i] = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s) * tau : 0.0f;
+      need_clamp |= s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
+      if (NG == 1 || i == (g & (NG - 1))) s_own = s32;
+    }
+    {
+      int64_t si = -1;
+      if (G == 32) si = row * 64 + 4 * a4 + g;
+      else if (G == 64) si = g < 2 ? row * 32 + 2 * a4 + g : -1;
+      else if (G == 128) si = g == 0 ? row * 16 + a4 : -1;
+      else si = (g == 0 && (a4 & 1) == 0) ? row * 8 + (a4 >> 1) : -1;
+      if (si >= 0) {
+        if (SCALE_F16) reinterpret_cast<_Float16*>(scales)[si] = (_Float16)s_own;
+        else reinterpret_cast<float*>(scales)[si] = s_own;
+      }
+    }
+    const bool clamp = __builtin_amdgcn_ballot_w64(need_clamp) != 0;
+    const float M = 12582920.0f;                 // 1.5 * 2^23 + 8
+    u32x4* cl = &code_lds[wib][0];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float k = kk[G == 32 ? m : G == 64 ? (m >> 1) : 0];
+      const f32x4 lo = acc[2 * m], hi = acc[2 * m + 1];
+      float rr[8] = {fmaf(lo[0], k, M), fmaf(lo[1], k, M), fmaf(lo[2], k, M), fmaf(lo[3], k, M),
+                     fmaf(hi[0], k, M), fmaf(hi[1], k, M), fmaf(hi[2], k, M), fmaf(hi[3], k, M)};
+      if (clamp) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rr[e] = __builtin_amdgcn_fmed3f(rr[e], M - 7.0f, M + 7.0f);
+      }
+      // dword 16 a + 4 m + g of the row: 16-byte block (a, m) at 4 a + (m ^ (a >> 2 & 3))
+      reinterpret_cast<uint32_t*>(cl)[4 * (4 * a4 + (m ^ ((a4 >> 2) & 3))) + g] = pack8(rr);
+    }
+    // lane i stores bytes 16 i .. 16 i + 15 of the row: block (i >> 2, i & 3)
+    const int ra = lane >> 2, rm = lane & 3;
+    const u32x4 out = cl[4 * ra + (rm ^ ((ra >> 2) & 3))];
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * (N / 2)) + lane);
+  };
+
+  int64_t row = wave;
+  if (row < rows) issue(row, 0);
+  if (row + nwaves < rows) issue(row + nwaves, 1);
+  for (int st = 0; row < rows; row += nwaves, st ^= 1) {
+    u32x4 b[4];
+    read_stage(st, row + nwaves < rows, b);
+    if (row + 2 * nwaves < rows) issue(row + 2 * nwaves, st);
+    process(row, b);
+  }
+}
+
+template <int G, bool SCALE_F16, bool OUT_F32>
+static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
+  int64_t blocks = (a.rows + 3) / 4;              // 4 waves per block, one row per wave
+  const int64_t cap = 256 * kMfmaBlocksPerCu;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32>), dim3((unsigned)blocks), dim3(256),
+                     0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
+                     a.scales, norm);
+}
+
+// bf16 rows of n = 2048 (m = 1): fp32 output or fused quantization.  Returns
+// false when the case belongs to another kernel.
+bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s) {
+  if (!a.x_bf16 || a.p != 2048 || a.m != 1) return false;
+  const float norm = (float)(1.0 / sqrt(2048.0));
+  if (a.y && !a.codes) {
+    launch_mfma<0, false, true>(a, norm, s);
+    return true;
+  }
+  if (!a.codes || a.y) return false;
+#define HR_MQ(G)                                                   \
+  case G:                                                          \
+    if (a.scale_f16) launch_mfma<G, true, false>(a, norm, s);      \
+    else launch_mfma<G, false, false>(a, norm, s);                 \
+    return true;
+  switch (a.group) {
+    HR_MQ(32)
+    HR_MQ(64)
+    HR_MQ(128)
+    HR_MQ(256)
+    default: return false;
+  }
+#undef HR_MQ
+}
+
+}  // namespace hr

@@ -61,6 +61,29 @@ def test_rotate_closed_forms():
     assert np.all(y[1, 1:] == 0.0)
 
 
+@pytest.mark.parametrize("rows", [1, 2, 3])
+def test_rotate_closed_forms_bf16(rows):
+    """bf16 input (the matrix-core path at n = 2048): a delta row gives d_0 / sqrt(n)
+    everywhere, the sign vector itself gives sqrt(n) e_0 with exact zeros; one to
+    three rows exercise the odd tail of the two-row step."""
+    hr = _hr()
+    n = 2048
+    d = hr_inputs.sign_vector(np.random.default_rng(6), n)
+    x = np.zeros((3, n), dtype=np.float32)
+    x[0, 0] = 1.0
+    x[1] = d
+    x[2, 5] = -2.0
+    xb = torch.from_numpy(x[:rows]).to(torch.bfloat16)
+    y = hr.rotate(xb.to(DEV), torch.from_numpy(d).to(DEV)).cpu().numpy()
+    np.testing.assert_allclose(y[0], d[0] / math.sqrt(n), rtol=1e-6)
+    if rows > 1:
+        assert abs(y[1, 0] - math.sqrt(n)) <= 1e-6 * math.sqrt(n)
+        assert np.all(y[1, 1:] == 0.0)
+    if rows > 2:
+        h5 = np.array([(-1) ** bin(i & 5).count("1") for i in range(n)], dtype=np.float64)
+        np.testing.assert_allclose(y[2], -2.0 * d[5] * h5 / math.sqrt(n), rtol=1e-6)
+
+
 def test_rotate_zero_rows():
     hr = _hr()
     x = torch.empty((0, 2048), dtype=torch.bfloat16, device=DEV)
@@ -69,8 +92,8 @@ def test_rotate_zero_rows():
 
 # ------------------------------------------------------- rotate + quantize
 
-@pytest.mark.parametrize("n,group", [(2048, 128), (2048, 32), (64, 32), (256, 64), (1024, 256),
-                                     (4096, 128), (16384, 128)])
+@pytest.mark.parametrize("n,group", [(2048, 128), (2048, 32), (2048, 64), (2048, 256), (64, 32),
+                                     (256, 64), (1024, 256), (4096, 128), (16384, 128)])
 @pytest.mark.parametrize("scale_mode", ["f16", "f32"])
 def test_rotate_quant(n, group, scale_mode):
     hr = _hr()
@@ -108,6 +131,24 @@ def test_rotate_quant_large_dynamic_range():
     codes, scales = hr.rotate_quant_int4(torch.from_numpy(x).to(DEV), group,
                                          torch.from_numpy(d).to(DEV))
     check_quant(codes.cpu().numpy(), scales.cpu().numpy(), oracle.hadamard.rht(x, d), group, "f16")
+
+
+@pytest.mark.parametrize("group", [32, 128, 256])
+def test_rotate_quant_large_dynamic_range_bf16(group):
+    """bf16 rows spanning many binades (matrix-core path), zero and tiny rows."""
+    hr = _hr()
+    n = 2048
+    rng = np.random.default_rng(13 + group)
+    x = (rng.standard_normal((67, n)) * np.exp2(rng.integers(-30, 10, size=(67, 1)))).astype(np.float32)
+    x[7] = 0.0
+    x[8] = 1e-30
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    d = hr_inputs.sign_vector(rng, n)
+    codes, scales = hr.rotate_quant_int4(xb.to(DEV), group, torch.from_numpy(d).to(DEV))
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.all(codes[7] == 0) and np.all(scales[7] == 0)
+    assert np.all(codes[8] == 0) and np.all(scales[8] == 0)
+    check_quant(codes, scales, oracle.hadamard.rht(xb.float().numpy(), d), group, "f16")
 
 
 # ---------------------------------------------------------------- mixed radix
