@@ -32,8 +32,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(HERE, "profiles")
 CSRC = os.path.join(HERE, "hadamard_rotation_int4_amd", "csrc")
 # sources that make up the headline kernel (its counters go stale when they change)
-MAIN_KERNEL_SOURCES = ("rht2048.hip", "fwht2048.h", "hr_device.h", "hr_internal.h")
-MAIN_KERNEL_NAME = "rht2048_kernel<true, 128, true, false>"
+MAIN_KERNEL_SOURCES = ("rht2048_mfma.hip", "fwht2048.h", "hr_device.h", "hr_internal.h")
+MAIN_KERNEL_NAME = "rht2048_mfma_kernel<128, true, false>"
 TRAFFIC_FILE = os.path.join(PROFILES, "rht_quant_bf16_65536x2048_g128.traffic.json")
 COPY_BYTES = 512 * 1024 * 1024       # calibration copy: reads and writes this many bytes
 
@@ -117,8 +117,8 @@ def cpu_baseline(target_s: float = 15.0):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time only the headline kernel")
     ap.add_argument("--profile-run", action="store_true",
@@ -304,8 +304,8 @@ def summarize_profile(d):
         f.write("\n".join(lines) + "\n")
     fetch = _read_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
     write = _read_csv(os.path.join(d, "write", "**", "*counter_collection.csv"))
-    kf, nk = _counter_per_dispatch(fetch, "rht2048_kernel", "FETCH_SIZE")
-    kw, _ = _counter_per_dispatch(write, "rht2048_kernel", "WRITE_SIZE")
+    kf, nk = _counter_per_dispatch(fetch, "rht2048_mfma_kernel<128, true, false>", "FETCH_SIZE")
+    kw, _ = _counter_per_dispatch(write, "rht2048_mfma_kernel<128, true, false>", "WRITE_SIZE")
     cf = cw = None
     nc = 0
     copy_kernel = None

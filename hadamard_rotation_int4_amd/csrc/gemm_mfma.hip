@@ -9,16 +9,15 @@
 // nibble.  x & 0xF0F0F0F0 turns a dword of 8 codes into 4 int8 bytes equal to
 // 16 * (odd codes), (x << 4) & 0xF0F0F0F0 into 16 * (even codes).  Both
 // operands get the same K permutation, so every int32 sum is exactly 256 times
-// the true group sum; the 1/256 is folded (exactly) into the W scale.
+// the true group sum; the 1/256 is applied (exactly) to the fp32 result.
 //
-// Prefill kernel: a 128x128 output tile per workgroup of 4 waves, 64x64 per
-// wave (4x4 v_mfma_i32_16x16x64_i8 tiles).  Each pipeline stage covers up to
-// 128 K values: the packed operands of the next stage are loaded into
-// registers while the current stage runs, then unpacked once into LDS in MFMA
-// operand order (lane chunk c of a 16-row block is 16 contiguous bytes, so a
-// wave's operand read is 1 KB contiguous and bank-conflict free).  After the
-// last stage of a group the wave converts its 64 group sums to fp32 and
-// accumulates them with sA * sW.
+// Prefill kernel (M > 16): a 128x128 output tile per workgroup of 4 waves,
+// 64x64 per wave as 2x2 v_mfma_i32_32x32x32_i8 tiles, stages of up to 128
+// codes unpacked once into LDS; the per-group scale fusion is described at
+// the kernel.  Measured on MI355X, vector-ALU work of one wave does not run
+// alongside the MFMAs of another wave on the same SIMD, while independent
+// vector instructions that follow a wave's own MFMA do; the kernel therefore
+// interleaves each wave's epilogue with its own MFMAs.
 //
 // Decode kernel (M <= 16): one 16x16 output tile per workgroup of 4 waves
 // that split K; operands go straight from global memory into registers, the
@@ -47,168 +46,269 @@ __device__ __forceinline__ float ld_scale(const void* p, int64_t idx) {
 
 constexpr int kBM = 128, kBN = 128;
 
-// LDS slot of chunk ch of row r in a [chunk][row] operand buffer.  The XOR
-// on the row keeps both access patterns free of bank conflicts: a store
-// wave writes 8 chunks of a few rows (s maps 8 chunks x 2 rows to 16 distinct
-// 16-byte bank groups), an MFMA read takes one chunk of 16 consecutive rows
-// (an XOR below 16 only permutes an aligned 16-row block).
-__device__ __forceinline__ int lds_slot(int ch, int r, int rows) {
-  const int s = 2 * (ch & 7) + ((ch >> 2) & 1);
-  return ch * rows + (r ^ s);
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// XOR applied to the row index of chunk pair q (chunks 2q, 2q + 1) in the
+// LDS operand buffers, laid out [chunk][128 rows] of 16-byte slots.  A
+// 16-byte store phase covers 8 or 16 lanes: rows r0 .. r0 + 16/PPR - 1 (or
+// half of them) times the PPR pieces of a row (PPR packed 16-byte pieces per
+// row and stage), writing chunk 2p (or 2p + 1) of piece p.  With the
+// constants {0, 6, 10, 12} (PPR = 4) or {0, 12} (PPR = 2) those writes hit
+// 16-byte bank groups that differ modulo 8 and modulo 16.  A read phase
+// takes one chunk of 8 or 16 consecutive rows, which an XOR below 16 only
+// permutes.  Both patterns are free of bank conflicts.
+template <int PPR>
+__device__ __forceinline__ constexpr int row_xor(int q) {
+  return PPR == 4 ? (q == 0 ? 0 : q == 1 ? 6 : q == 2 ? 10 : 12) : (q == 0 ? 0 : 12);
 }
 
+template <int V>
+struct IntC { static constexpr int value = V; };
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+// Prefill kernel.  A 128x128 output tile per workgroup of 4 waves, 64x64 per
+// wave as 2x2 tiles of v_mfma_i32_32x32x32_i8.  Per pipeline stage of KS
+// codes: every thread buffer-loads 16-byte pieces of packed rows (PPR lanes
+// cover the bytes a row holds for a stage), unpacks them once and stores them
+// to LDS in operand order; the waves read their fragments with one
+// ds_read_b128 per 32-row block and K-step.  Lane l of a fragment holds row
+// l % 32 and chunk 2s + l / 32 of K-step s, i.e. codes 32 s .. 32 s + 31 of
+// the stage, in the same (permuted) order for both operands.
+//
+// Group epilogue with fp16 scales: the outer product sA (x) sW of the group
+// is itself one v_mfma_f32_32x32x16_f16 per 32x32 tile (lane l < 32 puts the
+// scale of row / column l in K slot 0, every other slot is zero; products of
+// two fp16 values are exact in fp32), so the vector ALU only converts the
+// int32 sums and runs one fma per output and group.  With fp32 scales the
+// product sA * sW is formed on the vector ALU.
+//
+// Overlap: each stage runs in two halves.  The first half issues the MFMAs
+// of the upper tiles (i = 0) while the vector ALU finishes the previous
+// group of the lower tiles (i = 1); the second half issues the lower tiles'
+// MFMAs while the upper tiles' group is converted and accumulated.  Every
+// tile's sums are consumed before its next group overwrites them, so no
+// second accumulator set is needed.  Group scales go through a 3-deep LDS
+// ring, so the lower tiles can still read the previous group's scales after
+// other waves have stored the next stage's.  Stages are unrolled in pairs so
+// that the LDS buffer of every access is a compile-time offset.
 template <int G, bool F16, bool WRITE_ACC>
 __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
-  constexpr int KS = G < 128 ? G : 128;   // K values per pipeline stage
-  constexpr int STEPS = KS / 64;          // MFMA K-steps per stage
-  constexpr int SPG = G / KS;             // stages per group
-  constexpr int CH = KS / 16;             // 16-code chunks per row per stage
-  constexpr int LOADS = kBM * CH / 256;   // packed 8-byte loads per thread per operand
-  // operand buffers in MFMA order: [buf][chunk][row] of 16 bytes
-  __shared__ v4i la[2][CH * kBM];
-  __shared__ v4i lw[2][CH * kBN];
-  __shared__ __attribute__((aligned(16))) float lsa[2][kBM];
-  __shared__ __attribute__((aligned(16))) float lsw[2][kBN];
+  constexpr int KS = G < 128 ? G : 128;   // codes per pipeline stage
+  constexpr int STEPS = KS / 32;          // MFMA K-steps per stage
+  constexpr int SPG = G / KS;             // stages per group (1 or 2)
+  constexpr int PPR = KS / 32;            // 16-byte packed pieces per row and stage
+  constexpr int LOADS = PPR;              // pieces per thread and stage (both operands)
+  constexpr int LPO = LOADS / 2;          // pieces per thread and operand
+  constexpr int OPB = (KS / 16) * 128 * 16;   // bytes of one operand stage in LDS
+  constexpr int LSC = 4 * OPB;            // byte offset of the scale ring
+  constexpr int SB = F16 ? 2 : 4;         // bytes per scale
+  __shared__ __attribute__((aligned(16))) char smem[4 * OPB + 3 * 1024];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const uint32_t hmask = h ? 0u : 0xFFFFFFFFu;
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int64_t n0 = (int64_t)blockIdx.x * kBN;
-  const int64_t K = g.K;
-  const int64_t rowb = K / 2;             // bytes per packed row
-  const int ngroups = (int)(K / G);
-  const int nstages = (int)(K / KS);
+  const int64_t rowb = g.K / 2;           // bytes per packed row
+  const int ngroups = (int)(g.K / G);
+  const int nstages = (int)(g.K / KS);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
 
-  float c[4][4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) c[i][j][v] = 0.0f;
-  v4i acc[4][4];
-
-  // per-thread packed-row offsets, fixed for the whole K loop (32-bit: a
-  // 128-row panel of packed operands is far below 2^31 bytes)
-  const uint8_t* __restrict__ abase = g.a + m0 * rowb;
-  const uint8_t* __restrict__ wbase = g.w + n0 * rowb;
-  uint32_t aoff[LOADS], woff[LOADS];
-  bool aval[LOADS];
+  // Packed operand panels and this thread's pieces: piece t of operand op is
+  // tile row srow + t' * 256 / PPR (t' = t mod LPO), 16-byte piece spc; A rows
+  // past M read row 0 of the panel instead (a valid address; never stored).
+  const __amdgpu_buffer_rsrc_t rs_a =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(g.a + m0 * rowb), 0, (int)(128 * rowb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_w =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(g.w + n0 * rowb), 0, (int)(128 * rowb), 0x00020000);
+  const int srow = tid / PPR, spc = tid % PPR;
+  int voff[LOADS];
 #pragma unroll
   for (int t = 0; t < LOADS; ++t) {
-    const int u = tid + 256 * t;
-    aval[t] = m0 + u / CH < g.M;
-    woff[t] = (uint32_t)((u / CH) * rowb + (u % CH) * 8);
-    // A rows past M read row 0 of the panel (a valid address) and are zeroed
-    aoff[t] = (uint32_t)((aval[t] ? u / CH : 0) * rowb + (u % CH) * 8);
+    const int r = srow + (t % LPO) * (256 / PPR);
+    const bool clamp = t < LPO && m0 + r >= g.M;
+    voff[t] = (clamp ? 0 : r) * (int)rowb + 16 * spc;
   }
-  // scale of this thread's row (threads 0-127: A rows, 128-255: W rows); the
-  // load is unconditional (a valid index even past M) so it never forces the
-  // wave to drain its outstanding loads, and the raw bits are converted when
-  // they are stored to LDS
-  const int64_t srow_raw = tid < kBM ? (m0 + tid) : (n0 + tid - kBM);
-  const bool sval = tid < kBM ? (srow_raw < g.M) : true;
-  const int64_t srow = sval ? srow_raw : 0;
-  const void* sbase = tid < kBM ? g.sa : g.sw;
-  const float smul = tid < kBM ? 1.0f : (1.0f / 256.0f);
+  // scale row of this thread: threads 0-127 (waves 0, 1) A rows, 128-255 W rows
+  const int64_t sr = tid < kBM ? (m0 + tid < g.M ? m0 + tid : m0) : n0 + tid - kBM;
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wave < 2 ? g.sa : g.sw), 0, 0x7FFFFFFF, 0x00020000);
+  const int svoff = (int)(sr * ngroups * SB);
 
-  uint2 pa[LOADS], pw[LOADS];
+  // LDS byte offsets: this thread's store slot (chunk 2 spc, row srow), and
+  // the fragment read slots of K-step ks (chunk 2 ks + h, row wm + l32 or
+  // wn + l32) within an operand stage
+  const int st_off = (2 * spc * 128 + (srow ^ row_xor<PPR>(spc))) * 16;
+  int rd_a[STEPS], rd_b[STEPS];
+#pragma unroll
+  for (int ks = 0; ks < STEPS; ++ks) {
+    rd_a[ks] = (h * 128 + wm + (l32 ^ row_xor<PPR>(ks))) * 16;
+    rd_b[ks] = OPB + (h * 128 + wn + (l32 ^ row_xor<PPR>(ks))) * 16;
+  }
+
+  v16f c[2][2];
+  v16i acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      c[i][j] = (v16f){};
+      acc[i][j] = (v16i){};
+    }
+
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  v4u pre[LOADS];
   uint32_t psc = 0;
   auto load_stage = [&](int s) {
-    const uint32_t soff = (uint32_t)s * (KS / 2);
+    const int so = s * (KS / 2);
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t)
+      pre[t] = __builtin_amdgcn_raw_buffer_load_b128(t < LPO ? rs_a : rs_w, voff[t], so, 0);
+    const int gso = (s / SPG) * SB;
+    psc = F16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs_s, svoff, gso, 0)
+              : __builtin_amdgcn_raw_buffer_load_b32(rs_s, svoff, gso, 0);
+  };
+  auto store_stage = [&](auto bufc, int ring) {
+    char* sb = smem + decltype(bufc)::value * 2 * OPB;
 #pragma unroll
     for (int t = 0; t < LOADS; ++t) {
-      const uint2 qa = *reinterpret_cast<const uint2*>(abase + aoff[t] + soff);
-      pa[t] = make_uint2(aval[t] ? qa.x : 0u, aval[t] ? qa.y : 0u);
-      pw[t] = *reinterpret_cast<const uint2*>(wbase + woff[t] + soff);
+      char* d = sb + (t / LPO) * OPB + (t % LPO) * (256 / PPR) * 16 + st_off;
+      *reinterpret_cast<v4i*>(d) = unpack16(make_uint2(pre[t].x, pre[t].y));
+      *reinterpret_cast<v4i*>(d + 2048) = unpack16(make_uint2(pre[t].z, pre[t].w));
     }
-    const int gi = s / SPG;      // scales of the group this stage belongs to
-    psc = F16 ? (uint32_t)reinterpret_cast<const uint16_t*>(sbase)[srow * ngroups + gi]
-              : reinterpret_cast<const uint32_t*>(sbase)[srow * ngroups + gi];
-  };
-  auto store_stage = [&](int s, int buf) {
-#pragma unroll
-    for (int t = 0; t < LOADS; ++t) {
-      const int u = tid + 256 * t;
-      const int row = u / CH, ch = u % CH;
-      la[buf][lds_slot(ch, row, kBM)] = unpack16(pa[t]);
-      lw[buf][lds_slot(ch, row, kBN)] = unpack16(pw[t]);
-    }
-    if (s % SPG == SPG - 1) {
-      const float v = F16 ? (float)__builtin_bit_cast(_Float16, (uint16_t)psc) : __uint_as_float(psc);
-      const float sc = sval ? v * smul : 0.0f;
-      if (tid < kBM) lsa[buf][tid] = sc;
-      else lsw[buf][tid - kBM] = sc;
-    }
+    *reinterpret_cast<uint32_t*>(smem + LSC + ring * 1024 + tid * 4) = psc;
   };
 
-  load_stage(0);
-  store_stage(0, 0);
-  __syncthreads();
-
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nstages) load_stage(s + 1);
+  // MFMAs of tiles (i, 0) and (i, 1) over one stage; the B fragments are read
+  // in the first half and kept for the second
+  auto mfma_half = [&](auto bufc, int i, bool zero_first, v4i (&bfr)[STEPS][2], bool read_b) {
+    const char* sb = smem + decltype(bufc)::value * 2 * OPB;
 #pragma unroll
     for (int ks = 0; ks < STEPS; ++ks) {
-      const bool first = (s % SPG == 0) && ks == 0;   // first K-step of a group
-      v4i af[4];
+      const v4i af = *reinterpret_cast<const v4i*>(sb + rd_a[ks] + (2 * ks * 128 + 32 * i) * 16);
+      if (read_b) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = la[buf][lds_slot(ks * 4 + (lane >> 4), wm + 16 * i + (lane & 15), kBM)];
+        for (int j = 0; j < 2; ++j)
+          bfr[ks][j] = *reinterpret_cast<const v4i*>(sb + rd_b[ks] + (2 * ks * 128 + 32 * j) * 16);
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i bf = lw[buf][lds_slot(ks * 4 + (lane >> 4), wn + 16 * j + (lane & 15), kBN)];
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = (zero_first && ks == 0)
+                        ? __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[ks][j], (v16i){}, 0, 0, 0)
+                        : __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[ks][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // group epilogue of tiles (i, 0) and (i, 1) with the scales in ring slot
+  // ring; lane holds acc[i][j][v] of row wm + 32 i + 8 (v / 4) + 4 h + v % 4,
+  // column wn + 32 j + l32
+  auto epilogue = [&](int i, int ring, int gi) {
+    const char* ls = smem + LSC + ring * 1024;
+    if (F16) {
+      const uint32_t ra = *reinterpret_cast<const uint32_t*>(ls + (wm + 32 * i + l32) * 4) & hmask;
+      const v4h sa = __builtin_bit_cast(v4h, (v2i){(int)ra, 0});
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][j] = first ? __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf, (v4i){0, 0, 0, 0}, 0, 0, 0)
-                            : __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf, acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t rw = *reinterpret_cast<const uint32_t*>(ls + (kBM + wn + 32 * j + l32) * 4) & hmask;
+        const v4h sw = __builtin_bit_cast(v4h, (v2i){(int)rw, 0});
+        const v16f p = __builtin_amdgcn_mfma_f32_32x32x8f16(sa, sw, (v16f){}, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c[i][j][v] = fmaf((float)acc[i][j][v], p[v], c[i][j][v]);
+      }
+    } else {
+      float sa[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 t4 = *reinterpret_cast<const uint4*>(ls + (wm + 32 * i + 8 * q + 4 * h) * 4);
+        sa[4 * q] = __uint_as_float(t4.x);
+        sa[4 * q + 1] = __uint_as_float(t4.y);
+        sa[4 * q + 2] = __uint_as_float(t4.z);
+        sa[4 * q + 3] = __uint_as_float(t4.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sw = *reinterpret_cast<const float*>(ls + (kBM + wn + 32 * j + l32) * 4);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c[i][j][v] = fmaf((float)acc[i][j][v], sa[v] * sw, c[i][j][v]);
       }
     }
-    if (s % SPG == SPG - 1) {
-      // group epilogue: lane holds acc[i][j][v] for row wm+16i+4(lane/16)+v,
-      // column wn+16j+lane%16
-      const int gi = s / SPG;
-      float sa[4][4], sw[4];
+    if (WRITE_ACC && gi >= 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 t4 = *reinterpret_cast<const float4*>(&lsa[buf][wm + 16 * i + 4 * (lane >> 4)]);
-        sa[i][0] = t4.x; sa[i][1] = t4.y; sa[i][2] = t4.z; sa[i][3] = t4.w;
-      }
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sw[j] = lsw[buf][wn + 16 * j + (lane & 15)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            c[i][j][v] = fmaf((float)acc[i][j][v], sa[i][v] * sw[j], c[i][j][v]);
-      if (WRITE_ACC) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int64_t row = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
-              const int64_t col = n0 + wn + 16 * j + (lane & 15);
-              if (row < g.M) g.group_acc[(row * g.N + col) * ngroups + gi] = acc[i][j][v] >> 8;
-            }
-      }
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int64_t col = n0 + wn + 32 * j + l32;
+          if (row < g.M) g.group_acc[(row * g.N + col) * ngroups + gi] = acc[i][j][v] >> 8;
+        }
     }
-    if (s + 1 < nstages) store_stage(s + 1, buf ^ 1);
-    __syncthreads();
-  }
+  };
 
+  // one pipeline stage; the stage's LDS buffer (s & 1) is the template
+  // constant, and with two stages per group so is its position in the group
+  auto stage = [&](int s, auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    constexpr int SUB = SPG == 1 ? 0 : B;
+    const int gi = s / SPG;
+    const int ring = s % 3;
+    // the last stage reloads itself (a valid address; the copy is never read)
+    load_stage(s + 1 < nstages ? s + 1 : s);
+    v4i bfr[STEPS][2];
+    // first half: fragment and scale reads, then each MFMA followed by a run
+    // of the lower tiles' epilogue on the vector ALU
+    mfma_half(bufc, 0, SUB == 0, bfr, true);
+    if (SUB == 0) epilogue(1, ring == 0 ? 2 : ring - 1, gi - 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 16, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 2 * STEPS + 2; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // second half: the lower tiles' MFMAs, the upper tiles' epilogue and the
+    // next stage's unpack and LDS stores
+    mfma_half(bufc, 1, SUB == 0, bfr, false);
+    if (SUB == SPG - 1) epilogue(0, ring, gi);
+    store_stage(IntC<B ^ 1>{}, ring == 2 ? 0 : ring + 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t row = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
+    for (int q = 0; q < 2 * STEPS + 2; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+
+  // ring slot 2 stands for the group before the first one: zero scales make
+  // the lower tiles' first (empty) epilogue add nothing
+  *reinterpret_cast<uint32_t*>(smem + LSC + 2 * 1024 + tid * 4) = 0u;
+  load_stage(0);
+  store_stage(IntC<0>{}, 0);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 <= nstages; s += 2) {
+    stage(s, IntC<0>{});
+    stage(s + 1, IntC<1>{});
+  }
+  if (s < nstages) stage(s, IntC<0>{});
+  epilogue(1, (nstages - 1) % 3, ngroups - 1);
+
+  // every int32 sum is 256 times the true one (both operands carry 16 x code)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
       if (row < g.M) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) g.c[row * g.N + n0 + wn + 16 * j + (lane & 15)] = c[i][j][v];
+        for (int j = 0; j < 2; ++j) g.c[row * g.N + n0 + wn + 32 * j + l32] = c[i][j][v] * (1.0f / 256.0f);
       }
     }
 }

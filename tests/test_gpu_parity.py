@@ -263,6 +263,31 @@ def test_gemm(M, N, K, group):
     assert torch.equal(c2, c)
 
 
+@pytest.mark.parametrize("M,N,K,group,scale_mode", [
+    (130, 256, 1024, 128, "f16"),    # two tiles of 128 x 256, ragged M
+    (300, 512, 768, 128, "f16"),     # ragged M over three tile rows
+    (257, 256, 512, 64, "f16"),      # 64-code stages
+    (200, 512, 1024, 256, "f16"),    # two stages per group
+    (1024, 2048, 512, 128, "f16"),   # 64 tiles: tile ranges per XCD
+    (1100, 1024, 256, 128, "f16"),   # 9 tile rows: a partial group of tile rows
+    (160, 256, 512, 128, "f32"),     # fp32 scales
+    (140, 512, 768, 64, "f32"),
+])
+def test_gemm_wide_tiles(M, N, K, group, scale_mode):
+    """N a multiple of 256 and M > 16: the 128 x 256 tile kernel."""
+    hr = _hr()
+    gi = hr_inputs.gemm_inputs(M=M, N=N, K=K, group=group, seed=700 + M)
+    sd = np.float16 if scale_mode == "f16" else np.float32
+    sa, sw = gi.a_scales.astype(sd), gi.w_scales.astype(sd)
+    t = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    c, acc = hr.w4a4_gemm(t(gi.a_codes), t(sa), t(gi.w_codes), t(sw), group, group_acc=True)
+    c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(gi.a_codes, sa, gi.w_codes, sw, group,
+                                                  return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
+    c2 = hr.w4a4_gemm(t(gi.a_codes), t(sa), t(gi.w_codes), t(sw), group)
+    assert torch.equal(c2, c)
+
+
 def test_gemm_fp32_scales_and_minus_eight():
     hr = _hr()
     M, N, K, group = 33, 128, 512, 128
