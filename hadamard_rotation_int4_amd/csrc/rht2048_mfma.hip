@@ -72,7 +72,7 @@ __device__ __forceinline__ float max_over_rows(float m) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-constexpr int kMfmaBlocksPerCu = 4;
+constexpr int kMfmaBlocksPerCu = 2;
 
 template <int G, bool SCALE_F16, bool OUT_F32>
 __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
@@ -205,9 +205,12 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
     float mr[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
+      // three-input maxima (v_max3_f32 with |.| modifiers): 4 ops for 8 values
       const f32x4 lo = acc[2 * m], hi = acc[2 * m + 1];
-      mr[m] = fmaxf(fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])), fmaxf(fabsf(lo[2]), fabsf(lo[3]))),
-                    fmaxf(fmaxf(fabsf(hi[0]), fabsf(hi[1])), fmaxf(fabsf(hi[2]), fabsf(hi[3]))));
+      const float m1 = fmaxf(fmaxf(fabsf(lo[0]), fabsf(lo[1])), fabsf(lo[2]));
+      const float m2 = fmaxf(fmaxf(fabsf(lo[3]), fabsf(hi[0])), fabsf(hi[1]));
+      const float m3 = fmaxf(fmaxf(m1, fabsf(hi[2])), fabsf(hi[3]));
+      mr[m] = fmaxf(m2, m3);
     }
     constexpr int NG = G == 32 ? 4 : G == 64 ? 2 : 1;   // groups per lane (shared by its 4 rows)
     float mg[NG];
