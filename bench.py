@@ -32,7 +32,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PROFILES = os.path.join(HERE, "profiles")
 CSRC = os.path.join(HERE, "hadamard_rotation_int4_amd", "csrc")
 # sources that make up the headline kernel (its counters go stale when they change)
-MAIN_KERNEL_SOURCES = ("rht2048_mfma.hip", "fwht2048.h", "hr_device.h", "hr_internal.h")
+MAIN_KERNEL_SOURCES = ("rht2048_mfma.hip", "mfma2048.h", "fwht2048.h", "hr_device.h", "hr_internal.h")
 MAIN_KERNEL_NAME = "rht2048_mfma_kernel<128, true, false>"
 TRAFFIC_FILE = os.path.join(PROFILES, "rht_quant_bf16_65536x2048_g128.traffic.json")
 COPY_BYTES = 512 * 1024 * 1024       # calibration copy: reads and writes this many bytes

@@ -169,6 +169,25 @@ def test_mixed_radix(m, p, group):
     check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, "f16")
 
 
+@pytest.mark.parametrize("m,group,with_signs,scale_mode", [(7, 128, True, "f16"), (4, 64, False, "f32"),
+                                                          (6, 256, True, "f32")])
+def test_mixed_radix_many_rows(m, group, with_signs, scale_mode):
+    """More rows than resident workgroups (each workgroup loops over rows),
+    with and without the sign diagonal, fp16 and fp32 scales."""
+    hr = _hr()
+    rows, p = 600, 2048
+    mi = hr_inputs.mixed_inputs(rows=rows, m=m, p=p, seed=350 + m)
+    signs = mi.signs if with_signs else np.ones_like(mi.signs)
+    xd = mi.x.to(DEV)
+    dd = torch.from_numpy(mi.signs).to(DEV) if with_signs else None
+    od = torch.from_numpy(mi.block).to(DEV)
+    y64 = oracle.mixed_radix.mixed_radix(mi.x.float().numpy(), signs, mi.block, p)
+    check_rotated(hr.rotate(xd, dd, od).cpu().numpy(), y64)
+    sd = torch.float16 if scale_mode == "f16" else torch.float32
+    codes, scales = hr.rotate_quant_int4(xd, group, dd, od, scale_dtype=sd)
+    check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, scale_mode)
+
+
 def test_mixed_radix_fp32_input_fp32_scales():
     hr = _hr()
     m, p, group = 5, 2048, 128
