@@ -19,9 +19,11 @@
 // vector instructions that follow a wave's own MFMA do; the kernel therefore
 // interleaves each wave's epilogue with its own MFMAs.
 //
-// Decode kernel (M <= 16): one 16x16 output tile per workgroup of 4 waves
-// that split K; operands go straight from global memory into registers, the
-// four partial tiles are summed through LDS.
+// Decode kernel (M <= 16): one 16x16 output tile per workgroup of 16 waves
+// that split K; operands are staged through LDS by global_load_lds, the
+// partial tiles are summed through LDS.
+#include <type_traits>
+
 #include "hr_internal.h"
 #include "hr_device.h"
 
@@ -314,81 +316,123 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
 }
 
 
-// M <= 16: each workgroup owns 16 output columns; its 4 waves split K into
-// quarters.  A wave issues the packed operand loads of up to 8 groups at once
-// (one memory round trip per chunk instead of one per group), runs
-// 16x16x64 MFMAs straight from registers, and the four partial tiles are
-// summed through LDS.  The workgroup's scales (16 rows of A and of W, all
-// groups) are staged in LDS once.
-constexpr int kDecMaxGroups = 256;
+// M <= 16: each workgroup owns 16 output columns; its 16 waves split K.  The
+// unit of work is a 64-byte run of a packed row (128 codes), or two runs when
+// a group spans two (G = 256); wave w takes units [w U / 16, (w + 1) U / 16).
+// Time here is set by how many bytes each CU pulls in (every workgroup also
+// reads the 16 rows of A), so a wave issues all loads of a chunk of CH runs
+// at once, with global_load_lds so that no registers wait on them: lane l of
+// a load reads row l / 4, 16-byte piece (l % 4) ^ ((l / 16) % 4) of the run,
+// four lanes covering 64 contiguous bytes.  A run feeds two
+// v_mfma_i32_16x16x64_i8 (codes 0..63 and 64..127); lane (r, j) = (lane % 16,
+// lane / 16) reads the 8 bytes of codes 16 j .. 16 j + 15 of that half (same K
+// slots for A and W, so group sums stay exact) with one ds_read_b64, and the
+// piece XOR spreads the 16 rows over all LDS banks.  The 16 partial 16 x 16
+// tiles are summed through LDS.
+constexpr int kDecWaves = 16;
+constexpr int kDecRuns = 2;      // runs per operand and chunk
+
+__device__ __forceinline__ void dec_lds_load16(const void* gp, void* lp) {
+  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+}
+__device__ __forceinline__ void dec_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int G, bool F16, bool WRITE_ACC>
-__global__ __launch_bounds__(256) void w4a4_gemm_decode_kernel(GemmArgs g) {
-  constexpr int STEPS = G / 64;
-  constexpr int GC = G == 256 ? 4 : 8;         // groups per load chunk
-  __shared__ float part[4][16 * 16];
-  __shared__ float ssa[kDecMaxGroups * 16];     // [group][row]
-  __shared__ float ssw[kDecMaxGroups * 16];     // [group][col], times 1/256
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmArgs g) {
+  constexpr int CH = kDecRuns;
+  constexpr int MPG = G / 64;                    // MFMAs per group
+  constexpr int RPU = G >= 128 ? G / 128 : 1;    // runs per unit of work
+  constexpr int GPC = 2 * CH / MPG;              // groups per chunk
+  typedef typename std::conditional<F16, _Float16, float>::type scale_t;
+  __shared__ float part[kDecWaves][16 * 16];
+  __shared__ __attribute__((aligned(16))) float sat[kDecWaves][GPC][16];   // [group][A row]
+  __shared__ __attribute__((aligned(16))) uint4 stage[kDecWaves][2][CH][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t K = g.K;
-  const int64_t rowb = K / 2;
-  const int ngroups = (int)(K / G);
-  for (int i = tid; i < 16 * ngroups; i += 256) {
-    const int r = i / ngroups, gg = i % ngroups;
-    ssa[gg * 16 + r] = r < g.M ? ld_scale<F16>(g.sa, (int64_t)r * ngroups + gg) : 0.0f;
-    ssw[gg * 16 + r] = ld_scale<F16>(g.sw, (n0 + r) * ngroups + gg) * (1.0f / 256.0f);
-  }
-  const int r = lane & 15;                      // A row / W column of this lane
+  const int64_t rowb = g.K / 2;
+  const int ngroups = (int)(g.K / G);
+  const int units = (int)(g.K / (128 * RPU));
+  const int rbeg = RPU * (wave * units / kDecWaves), rend = RPU * ((wave + 1) * units / kDecWaves);
   const bool arow = r < g.M;
-  const uint8_t* pa = g.a + (int64_t)(arow ? r : 0) * rowb;
-  const uint8_t* pw = g.w + (n0 + r) * rowb;
-  const int gpw = ngroups / 4;                  // groups per wave
-  const int gbeg = wave * gpw;
+  // loads: row l / 4, piece (l % 4) ^ ((l / 16) % 4)
+  const int lrow = lane >> 2, lpiece = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint8_t* la = g.a + (int64_t)(lrow < g.M ? lrow : 0) * rowb + 16 * lpiece;
+  const uint8_t* lw = g.w + (n0 + lrow) * rowb + 16 * lpiece;
+  // reads, half h of a run: piece 2 h + j / 2, byte 8 (j % 2) of it
+  const uint32_t rd0 = 64 * r + 16 * ((0 + (j >> 1)) ^ ((r >> 2) & 3)) + 8 * (j & 1);
+  const uint32_t rd1 = 64 * r + 16 * ((2 + (j >> 1)) ^ ((r >> 2) & 3)) + 8 * (j & 1);
+  const int64_t sa_row = (int64_t)(arow ? r : 0) * ngroups, sw_row = (n0 + r) * ngroups;
   float c[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  __syncthreads();
-  for (int gc = 0; gc < gpw; gc += GC) {
-    uint2 qa[GC * STEPS], qw[GC * STEPS];
+  for (int r0 = rbeg; r0 < rend; r0 += CH) {
+    const int nr = rend - r0 < CH ? rend - r0 : CH;    // runs in this chunk (>= 1)
+    const int g0 = r0 * 128 / G;                       // first group of the chunk
+    const int ng = (nr * 128 + G - 1) / G;             // groups in this chunk
+    // every load is issued (indices past the chunk repeat its last run or
+    // group, in bounds) so that none waits behind a branch
+    scale_t sab[GPC], swb[GPC];
 #pragma unroll
-    for (int t = 0; t < GC * STEPS; ++t) {
-      // groups past the wave's range reload its last group (never used)
-      const int gg = gbeg + (gc + t / STEPS < gpw ? gc + t / STEPS : gpw - 1);
-      const int64_t off = ((int64_t)gg * G + 64 * (t % STEPS) + 16 * (lane >> 4)) / 2;
-      const uint2 q = *reinterpret_cast<const uint2*>(pa + off);
-      qa[t] = make_uint2(arow ? q.x : 0u, arow ? q.y : 0u);
-      qw[t] = *reinterpret_cast<const uint2*>(pw + off);
+    for (int u = 0; u < GPC; ++u) {
+      const int uu = u < ng ? u : ng - 1;
+      sab[u] = reinterpret_cast<const scale_t*>(g.sa)[sa_row + g0 + uu];
+      swb[u] = reinterpret_cast<const scale_t*>(g.sw)[sw_row + g0 + uu];
     }
 #pragma unroll
-    for (int u = 0; u < GC; ++u) {
-      if (gc + u >= gpw) break;
-      const int gi = gbeg + gc + u;
+    for (int t = 0; t < CH; ++t) {
+      const int64_t off = (int64_t)(r0 + (t < nr ? t : nr - 1)) * 64;
+      dec_lds_load16(la + off, &stage[wave][0][t][0]);
+      dec_lds_load16(lw + off, &stage[wave][1][t][0]);
+    }
+    dec_wait_loads();
+    // A scales transposed through this wave's LDS: lane reads rows 4 j .. 4 j + 3
+    if (j == 0) {
+#pragma unroll
+      for (int u = 0; u < GPC; ++u)
+        if (u < ng) sat[wave][u][r] = arow ? (float)sab[u] : 0.0f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const char* sta = reinterpret_cast<const char*>(&stage[wave][0][0][0]);
+    const char* stw = reinterpret_cast<const char*>(&stage[wave][1][0][0]);
+#pragma unroll
+    for (int u = 0; u < GPC; ++u) {
+      if (u >= ng) break;
       v4i acc = (v4i){0, 0, 0, 0};
 #pragma unroll
-      for (int t = 0; t < STEPS; ++t)
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack16(qa[u * STEPS + t]),
-                                                    unpack16(qw[u * STEPS + t]), acc, 0, 0, 0);
-      // lane holds rows 4*(lane/16)+v of column n0 + lane%16
-      const float sw = ssw[gi * 16 + (lane & 15)];
-      const float4 sa4 = *reinterpret_cast<const float4*>(&ssa[gi * 16 + 4 * (lane >> 4)]);
-      const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
+      for (int m = u * MPG; m < (u + 1) * MPG; ++m) {
+        const uint32_t o = 1024u * (m >> 1) + ((m & 1) ? rd1 : rd0);
+        const uint2 pa = *reinterpret_cast<const uint2*>(sta + o);
+        const uint2 pw = *reinterpret_cast<const uint2*>(stw + o);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+            unpack16(make_uint2(arow ? pa.x : 0u, arow ? pa.y : 0u)), unpack16(pw), acc, 0, 0, 0);
+      }
+      // lane holds rows 4 j + v of column n0 + r
+      const float sw = (float)swb[u] * (1.0f / 256.0f);
+      const float4 s4 = *reinterpret_cast<const float4*>(&sat[wave][u][4 * j]);
+      const float sar[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        c[v] = fmaf((float)acc[v], sa[v] * sw, c[v]);
+        c[v] = fmaf((float)acc[v], sar[v] * sw, c[v]);
         if (WRITE_ACC) {
-          const int row = 4 * (lane >> 4) + v;
+          const int row = 4 * j + v;
           if (row < g.M)
-            g.group_acc[((int64_t)row * g.N + n0 + (lane & 15)) * ngroups + gi] = acc[v] >> 8;
+            g.group_acc[((int64_t)row * g.N + n0 + r) * ngroups + g0 + u] = acc[v] >> 8;
         }
       }
     }
+    __builtin_amdgcn_wave_barrier();
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v) part[wave][(4 * (lane >> 4) + v) * 16 + (lane & 15)] = c[v];
+  for (int v = 0; v < 4; ++v) part[wave][(4 * j + v) * 16 + r] = c[v];
   __syncthreads();
-  {
-    const int e = tid;                      // 256 outputs, one per thread
-    const int row = e >> 4, col = e & 15;
-    if (row < g.M)
-      g.c[(int64_t)row * g.N + n0 + col] = part[0][e] + part[1][e] + part[2][e] + part[3][e];
+  if (tid < 256) {
+    const int row = tid >> 4, col = tid & 15;
+    if (row < g.M) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) s += part[w][tid];
+      g.c[(int64_t)row * g.N + n0 + col] = s;
+    }
   }
 }
 
@@ -396,7 +440,7 @@ template <int G, bool F16, bool WRITE_ACC>
 static void launch_g(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 16) {
     hipLaunchKernelGGL((w4a4_gemm_decode_kernel<G, F16, WRITE_ACC>), dim3((unsigned)(a.N / 16)),
-                       dim3(256), 0, s, a);
+                       dim3(kDecWaves * 64), 0, s, a);
   } else {
     const dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM));
     hipLaunchKernelGGL((w4a4_gemm_tile_kernel<G, F16, WRITE_ACC>), grid, dim3(256), 0, s, a);
@@ -412,13 +456,12 @@ static void launch_dt(const GemmArgs& a, hipStream_t s) {
   }
 }
 
-// Tiled kernels need N % 128 == 0 (prefill) or K % (4 * group) == 0 and at
-// most 256 groups (decode: each wave's quarter of K is whole groups and the
-// scales fit in LDS); other shapes go to the simple kernel.
+// The prefill kernel needs N % 128 == 0; the decode kernel takes every shape
+// the library accepts (N % 64 == 0, K a multiple of 256 and of the group).
+// Other shapes go to the simple kernel.
 bool launch_gemm_mfma(const GemmArgs& a, hipStream_t s) {
   const bool decode = a.M <= 16;
   if (!decode && a.N % kBN) return false;
-  if (decode && (a.K % (4 * (int64_t)a.group) || a.K / a.group > kDecMaxGroups)) return false;
   switch (a.group) {
     case 64: launch_dt<64>(a, s); return true;
     case 128: launch_dt<128>(a, s); return true;

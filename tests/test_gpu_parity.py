@@ -307,6 +307,29 @@ def test_gemm_wide_tiles(M, N, K, group, scale_mode):
     assert torch.equal(c2, c)
 
 
+@pytest.mark.parametrize("M,N,K,group,scale_mode", [
+    (1, 64, 256, 256, "f16"),       # one group: a single wave of eight has work
+    (16, 128, 768, 256, "f16"),     # three groups over eight waves
+    (12, 128, 2560, 128, "f16"),    # 20 groups: two or three per wave
+    (7, 192, 4096, 64, "f32"),      # eight 32-byte runs per wave, fp32 scales
+    (16, 64, 16384, 64, "f16"),     # 32 groups per wave: four load chunks
+    (3, 256, 1536, 256, "f32"),     # two loads per group
+])
+def test_gemm_decode_shapes(M, N, K, group, scale_mode):
+    """M <= 16: the decode kernel over group counts that do not divide evenly."""
+    hr = _hr()
+    gi = hr_inputs.gemm_inputs(M=M, N=N, K=K, group=group, seed=900 + K + M)
+    sd = np.float16 if scale_mode == "f16" else np.float32
+    sa, sw = gi.a_scales.astype(sd), gi.w_scales.astype(sd)
+    t = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    c, acc = hr.w4a4_gemm(t(gi.a_codes), t(sa), t(gi.w_codes), t(sw), group, group_acc=True)
+    c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(gi.a_codes, sa, gi.w_codes, sw, group,
+                                                  return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
+    c2 = hr.w4a4_gemm(t(gi.a_codes), t(sa), t(gi.w_codes), t(sw), group)
+    assert torch.equal(c2, c)
+
+
 def test_gemm_fp32_scales_and_minus_eight():
     hr = _hr()
     M, N, K, group = 33, 128, 512, 128
