@@ -189,6 +189,31 @@ def gemm_inputs(M: int = 4096, N: int = 4096, K: int = 4096, group: int = 128,
 
 
 @dataclass
+class GemmW4A8Inputs:
+    a_codes: np.ndarray    # int8 [M][K], one code per element in -127..127
+    a_scales: np.ndarray   # fp16 [M][K/G]
+    w_codes: np.ndarray    # uint8 [N][K/2]
+    w_scales: np.ndarray   # fp16 [N][K/G]
+    M: int
+    N: int
+    K: int
+    group: int
+
+
+def gemm_w4a8_inputs(M: int = 4096, N: int = 4096, K: int = 4096, group: int = 128,
+                     seed: int = SEED_GEMM) -> GemmW4A8Inputs:
+    """Draw order: W codes, W scales (the same draws as gemm_inputs, so the
+    weight operand matches the W4A4 workload), then A int8 codes uniform in
+    -127..127, then A scales."""
+    rng = _rng(seed)
+    w_codes = random_packed_codes(rng, N, K)
+    w_scales = random_scales_f16(rng, N, K // group)
+    a_codes = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    a_scales = random_scales_f16(rng, M, K // group, 0.0001, 0.005)
+    return GemmW4A8Inputs(a_codes, a_scales, w_codes, w_scales, M, N, K, group)
+
+
+@dataclass
 class ProbeInputs:
     a: np.ndarray          # fp32 [M][K] activations with outlier channels
     b: np.ndarray          # fp32 [K][N] weights

@@ -1,4 +1,4 @@
-"""Oracle: W4A4 GEMM on packed int4 codes with per-group scales.
+"""Oracle: W4A4 and W4A8 GEMMs on int4 weight codes with per-group scales.
 
 Test infrastructure only.
 
@@ -12,7 +12,11 @@ Reading: C = A W^T with both operands K-contiguous packed int4 codes,
     acc[m][n][g] = sum_{k in group g} a[m][k] * w[n][k]      (exact integer)
     C[m][n]      = fl32( sum_g sA[m][g] * sW[n][g] * acc[m][n][g] )  (fp64 sum)
 The integer sums are computed with an fp64 matrix product, which is exact here
-(|a|, |w| <= 8 and G <= 4096 keep every partial sum far below 2^53).
+(|a| <= 128, |w| <= 8 and G <= 4096 keep every partial sum far below 2^53).
+
+W4A8 (same page, Method and Results: the "W4A8 (act8/wt4)" rows, int8
+activations against int4 weights): the same two formulas with A held as one
+int8 code per element instead of packed nibbles.
 """
 from __future__ import annotations
 
@@ -25,8 +29,12 @@ def group_sums(a_packed, w_packed, group: int, rows=None) -> np.ndarray:
     """Exact per-group integer sums, int64 [len(rows)][N][K/G].
 
     rows: optional index array of A rows to compute (all rows if None)."""
-    a = unpack_int4(a_packed).astype(np.float64)
-    w = unpack_int4(w_packed).astype(np.float64)
+    return _group_sums(unpack_int4(a_packed), unpack_int4(w_packed), group, rows)
+
+
+def _group_sums(a_codes, w_codes, group: int, rows=None) -> np.ndarray:
+    a = np.asarray(a_codes).astype(np.float64)
+    w = np.asarray(w_codes).astype(np.float64)
     if rows is not None:
         a = a[np.asarray(rows)]
     K = a.shape[1]
@@ -47,6 +55,21 @@ def w4a4_gemm(a_packed, a_scales, w_packed, w_scales, group: int, rows=None,
     Also returns, when return_sums, the fp64 per-element bound
     sum_g |sA sW acc_g| used to judge the fp32 result."""
     acc = group_sums(a_packed, w_packed, group, rows)
+    return _scale_sum(acc, a_scales, w_scales, rows, return_sums)
+
+
+def w4a8_gemm(a_codes, a_scales, w_packed, w_scales, group: int, rows=None,
+              return_sums: bool = False):
+    """W4A8: A int8 codes [M][K] (one per element), W packed int4 [N][K/2].
+    Returns as w4a4_gemm."""
+    a = np.asarray(a_codes)
+    if a.dtype != np.int8:
+        raise ValueError("a_codes must be int8")
+    acc = _group_sums(a, unpack_int4(w_packed), group, rows)
+    return _scale_sum(acc, a_scales, w_scales, rows, return_sums)
+
+
+def _scale_sum(acc, a_scales, w_scales, rows, return_sums):
     sa = np.asarray(a_scales).astype(np.float64)
     if rows is not None:
         sa = sa[np.asarray(rows)]

@@ -128,3 +128,69 @@ def test_probe_trends(probe_means):
     assert m[("W8A8", "none", 32)] < m[("W8A8", "none", 128)]
     # W8A8 is a few percent at most
     assert 0.5 < m[("W8A8", "none", 128)] < 3.5
+
+
+# ---------------------------------------------------------------- W4A8 oracle
+
+def test_w4a8_brute_force_tiny():
+    """Loops over every product against the matrix form, int8 activations."""
+    rng = np.random.default_rng(11)
+    M, N, K, G = 3, 5, 32, 8
+    a = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    w = rng.integers(-8, 8, size=(N, K))
+    sa = rng.uniform(0.0001, 0.005, size=(M, K // G)).astype(np.float16)
+    sw = rng.uniform(0.001, 0.05, size=(N, K // G)).astype(np.float16)
+    c, acc, bound = oracle.gemm.w4a8_gemm(a, sa, oracle.quant.pack_int4(w), sw, G, return_sums=True)
+    cb, accb = _brute_gemm(a, sa, w, sw, G)
+    assert np.array_equal(acc, accb)
+    np.testing.assert_allclose(c, cb, rtol=1e-6, atol=1e-12)
+    assert np.all(bound >= np.abs(c) * (1 - 1e-6))
+
+
+def test_w4a8_extreme_codes_exact():
+    """-127 * -8 over a whole 256-code group: the largest group sum magnitude."""
+    K, G = 512, 256
+    a = np.full((2, K), -127, dtype=np.int8)
+    a[1, :] = 127
+    w = np.full((3, K), -8)
+    ones_a = np.ones((2, K // G), dtype=np.float16)
+    ones_w = np.ones((3, K // G), dtype=np.float16)
+    c, acc, _ = oracle.gemm.w4a8_gemm(a, ones_a, oracle.quant.pack_int4(w), ones_w, G, return_sums=True)
+    assert acc[0, 0, 0] == 127 * 8 * 256 and acc[1, 2, 1] == -127 * 8 * 256
+    assert c[0, 1] == 2 * 127 * 8 * 256
+
+
+def test_w4a8_on_int4_range_equals_w4a4():
+    """Activation codes inside -7..7 held as int8 give the W4A4 result."""
+    gi = hr_inputs.gemm_inputs(M=7, N=32, K=512, group=128, seed=21)
+    a8 = oracle.quant.unpack_int4(gi.a_codes)
+    c4, acc4, _ = oracle.gemm.w4a4_gemm(gi.a_codes, gi.a_scales, gi.w_codes, gi.w_scales, 128,
+                                        return_sums=True)
+    c8, acc8, _ = oracle.gemm.w4a8_gemm(a8, gi.a_scales, gi.w_codes, gi.w_scales, 128,
+                                        return_sums=True)
+    assert np.array_equal(acc4, acc8) and np.array_equal(c4, c8)
+
+
+def test_w4a8_unit_scales_is_integer_matmul():
+    rng = np.random.default_rng(12)
+    M, N, K = 4, 6, 256
+    a = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    w = rng.integers(-8, 8, size=(N, K))
+    c = oracle.gemm.w4a8_gemm(a, np.ones((M, 1), np.float16), oracle.quant.pack_int4(w),
+                              np.ones((N, 1), np.float16), K)
+    assert np.array_equal(c.astype(np.int64), a.astype(np.int64) @ w.astype(np.int64).T)
+
+
+def test_w4a8_rejects_packed_activations():
+    gi = hr_inputs.gemm_inputs(M=2, N=4, K=256)
+    with pytest.raises(ValueError):
+        oracle.gemm.w4a8_gemm(gi.a_codes, gi.a_scales, gi.w_codes, gi.w_scales, 128)
+
+
+def test_w4a8_inputs_ranges():
+    gi = hr_inputs.gemm_w4a8_inputs(M=8, N=16, K=512)
+    assert gi.a_codes.dtype == np.int8 and gi.a_codes.min() >= -127 and gi.a_codes.max() <= 127
+    w = oracle.quant.unpack_int4(gi.w_codes)
+    assert w.min() >= -7 and w.max() <= 7
+    g4 = hr_inputs.gemm_inputs(M=8, N=16, K=512)
+    assert np.array_equal(gi.w_codes, g4.w_codes) and np.array_equal(gi.w_scales, g4.w_scales)

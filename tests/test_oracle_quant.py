@@ -62,6 +62,16 @@ def test_eight_bit_qmax():
     assert codes.tolist() == [[127, 64, -1, 0]]
 
 
+def test_eight_bit_ties_away_and_fp16_scale():
+    """absmax 127 * 2^-7 gives the exact scale 2^-7 (also exact in fp16); 10.5 and
+    -3.5 steps are exact ties and round away from zero."""
+    s = 2.0 ** -7
+    y = np.array([[-127 * s, 10.5 * s, -3.5 * s, 0.0, 126.49 * s, 0.5 * s, -0.49 * s, 2 * s]])
+    codes, scales, s_used = Q.quantize_groups(y, 8, "f16", bits=8)
+    assert scales.dtype == np.float16 and float(scales[0, 0]) == s and float(s_used[0, 0]) == s
+    assert codes.tolist() == [[-127, 11, -4, 0, 126, 1, 0, 2]]
+
+
 def test_pack_nibble_order():
     assert Q.pack_int4(np.array([[1, -1]])).tolist() == [[0xF1]]
     assert Q.pack_int4(np.array([[-7, 7]])).tolist() == [[0x79]]
