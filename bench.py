@@ -204,6 +204,15 @@ def main(argv=None):
                                                     "frac_hbm": b32 / ms32 / 1e6 / HBM_PEAK_GBS,
                                                     "bytes": b32}
         del s32
+        # int8 activation codes for the W4A8 GEMM (one byte per code)
+        c8 = [torch.empty((ROWS, N), dtype=torch.int8, device=dev) for _ in range(nbuf)]
+        ms8 = _timed(lambda i: hr.rotate_quant_int8(xs[i], GROUP, d, codes=c8[i], scales=scales[i]),
+                     args.steps, args.warmup, nbuf)
+        b8 = ROWS * N * 2 + ROWS * N + ROWS * (N // GROUP) * 2
+        kernels["rht_quant_int8_bf16_65536x2048_g128"] = {"ms": ms8, "GB/s": b8 / ms8 / 1e6,
+                                                          "frac_hbm": b8 / ms8 / 1e6 / HBM_PEAK_GBS,
+                                                          "bytes": b8}
+        del c8
         yf = torch.empty((ROWS, N), dtype=torch.float32, device=dev)
         msr = _timed(lambda i: hr.rotate(xs[i], d, out=yf), args.steps, args.warmup, nbuf)
         br = ROWS * N * 2 + ROWS * N * 4
@@ -267,6 +276,22 @@ def main(argv=None):
             ops = 2 * M * 4096 * 4096
             byts = M * 2048 + 4096 * 2048 + (M + 4096) * 32 * 2 + M * 4096 * 4
             kernels[f"w4a4_gemm_{M}x4096x4096_g128"] = {
+                "ms": msg, "TOPS": ops / msg / 1e9, "frac_int8_peak": ops / msg / 1e9 / INT8_PEAK_TOPS,
+                "GB/s": byts / msg / 1e6, "ops": ops, "bytes": byts,
+                "timing": "eager launches" if M > 16 else "HIP graph of 20 launches, replayed"}
+
+        # W4A8 GEMM: int8 activations, the same int4 weights
+        for M in (4096, 16):
+            gi = hr_inputs.gemm_w4a8_inputs(M=M)
+            t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+            ad, sad, wd, swd = t(gi.a_codes), t(gi.a_scales), t(gi.w_codes), t(gi.w_scales)
+            cg = torch.empty((M, 4096), dtype=torch.float32, device=dev)
+            timer = _timed if M > 16 else _timed_graph
+            msg = timer(lambda i: hr.w4a8_gemm(ad, sad, wd, swd, 128, out=cg), args.steps,
+                        args.warmup)
+            ops = 2 * M * 4096 * 4096
+            byts = M * 4096 + 4096 * 2048 + (M + 4096) * 32 * 2 + M * 4096 * 4
+            kernels[f"w4a8_gemm_{M}x4096x4096_g128"] = {
                 "ms": msg, "TOPS": ops / msg / 1e9, "frac_int8_peak": ops / msg / 1e9 / INT8_PEAK_TOPS,
                 "GB/s": byts / msg / 1e6, "ops": ops, "bytes": byts,
                 "timing": "eager launches" if M > 16 else "HIP graph of 20 launches, replayed"}

@@ -1,6 +1,6 @@
 """Python binding of libhr.so (ctypes): randomized Hadamard rotation, fused
-int4 quantization, HARP-style butterfly, int4 dequant and the W4A4 GEMM on
-MI355X (gfx950).
+int4 / int8 quantization, HARP-style butterfly, int4 dequant and the W4A4 /
+W4A8 GEMMs on MI355X (gfx950).
 
 Argument marshalling only: every step runs in the library's HIP kernels on
 torch's current stream.  Tensors must be CUDA tensors, contiguous, of the
@@ -15,8 +15,8 @@ import os
 
 import torch
 
-__all__ = ["HRError", "rotate", "rotate_quant_int4", "butterfly_coeffs", "butterfly_apply",
-           "dequant_int4", "w4a4_gemm", "lib", "LIB_PATH", "SYMBOLS",
+__all__ = ["HRError", "rotate", "rotate_quant_int4", "rotate_quant_int8", "butterfly_coeffs",
+           "butterfly_apply", "dequant_int4", "w4a4_gemm", "w4a8_gemm", "lib", "LIB_PATH", "SYMBOLS",
            "HR_OK", "HR_EINVAL", "HR_EUNSUPPORTED", "HR_EDEVICE", "HR_F32", "HR_BF16", "HR_F16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhr.so")
@@ -33,10 +33,12 @@ SYMBOLS = {
     "hr_last_error": (ctypes.c_char_p, []),
     "hr_rotate": (_i32, [_vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, _vp]),
     "hr_rotate_quant_int4": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
+    "hr_rotate_quant_int8": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
     "hr_butterfly_coeffs": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "hr_butterfly_apply": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
     "hr_dequant_int4": (_i32, [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp]),
     "hr_w4a4_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "hr_w4a8_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
 }
 
 
@@ -123,6 +125,24 @@ def rotate_quant_int4(x: torch.Tensor, group: int, signs: torch.Tensor | None = 
     return codes, scales
 
 
+def rotate_quant_int8(x: torch.Tensor, group: int, signs: torch.Tensor | None = None,
+                      block: torch.Tensor | None = None, scale_dtype=torch.float16,
+                      codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Fused rotation + per-group int8 quantization (hr_rotate_quant_int8).
+    Returns (codes int8 [rows][n], scales [rows][n/group] of scale_dtype)."""
+    rows, n = x.shape
+    m = 1 if block is None else int(block.shape[0])
+    if codes is None:
+        codes = torch.empty((rows, n), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, n // group), dtype=scale_dtype, device=x.device)
+    _check(lib.hr_rotate_quant_int8(_ptr(x), _dtype_code(x.dtype), rows, n, m, _ptr(signs),
+                                    _ptr(block), group, _ptr(codes), _ptr(scales),
+                                    _dtype_code(scales.dtype), _stream(x.device)),
+           "hr_rotate_quant_int8")
+    return codes, scales
+
+
 def butterfly_coeffs(angles: torch.Tensor, precondition: bool = False) -> torch.Tensor:
     """Per-pair coefficient table [log2 n][n/2][2] fp32 from angles [log2 n][n/2]."""
     L, half = angles.shape
@@ -186,4 +206,25 @@ def w4a4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tens
     _check(lib.hr_w4a4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
                             _dtype_code(a_scales.dtype), M, N, K, group, _ptr(c), _ptr(acc),
                             _stream(a_codes.device)), "hr_w4a4_gemm")
+    return (c, acc) if group_acc else c
+
+
+def w4a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+              w_scales: torch.Tensor, group: int, out: torch.Tensor | None = None,
+              group_acc: bool = False):
+    """C = A W^T with int8 activation codes a_codes [M][K] and packed int4
+    weights (hr_w4a8_gemm).  Returns as w4a4_gemm."""
+    if a_codes.dtype != torch.int8:
+        raise TypeError("a_codes must be int8 [M][K]")
+    M, K = a_codes.shape
+    N = int(w_codes.shape[0])
+    if a_scales.dtype != w_scales.dtype:
+        raise TypeError("a_scales and w_scales must share a dtype")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    acc = None
+    if group_acc:
+        acc = torch.empty((M, N, K // group), dtype=torch.int32, device=a_codes.device)
+    _check(lib.hr_w4a8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
+                            _dtype_code(a_scales.dtype), M, N, K, group, _ptr(c), _ptr(acc),
+                            _stream(a_codes.device)), "hr_w4a8_gemm")
     return (c, acc) if group_acc else c

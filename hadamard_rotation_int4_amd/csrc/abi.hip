@@ -101,11 +101,12 @@ int32_t hr_rotate(const void* x, int32_t x_dtype, float* y, int64_t rows, int32_
   return from_hip(hr::launch_rht(a, static_cast<hipStream_t>(stream)), "hr_rotate");
 }
 
-int32_t hr_rotate_quant_int4(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t m,
-                             const int8_t* signs, const float* block, int32_t group,
-                             uint8_t* codes, void* scales, int32_t scale_dtype, void* stream) {
+// Shared body of hr_rotate_quant_int4 and hr_rotate_quant_int8.
+static int32_t rotate_quant(const char* fn, int bits, const void* x, int32_t x_dtype, int64_t rows,
+                            int32_t n, int32_t m, const int8_t* signs, const float* block,
+                            int32_t group, uint8_t* codes, void* scales, int32_t scale_dtype,
+                            void* stream) {
   int p = 0;
-  const char* fn = "hr_rotate_quant_int4";
   const int32_t st = check_rotation(fn, x, x_dtype, rows, n, m, signs, block, &p);
   if (st) return st;
   if ((!codes || !scales) && rows > 0)
@@ -128,9 +129,24 @@ int32_t hr_rotate_quant_int4(const void* x, int32_t x_dtype, int64_t rows, int32
   a.block = block;
   a.group = group;
   a.codes = codes;
+  a.bits = bits;
   a.scales = scales;
   a.scale_f16 = scale_dtype == HR_F16;
   return from_hip(hr::launch_rht(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t hr_rotate_quant_int4(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t m,
+                             const int8_t* signs, const float* block, int32_t group,
+                             uint8_t* codes, void* scales, int32_t scale_dtype, void* stream) {
+  return rotate_quant("hr_rotate_quant_int4", 4, x, x_dtype, rows, n, m, signs, block, group, codes,
+                      scales, scale_dtype, stream);
+}
+
+int32_t hr_rotate_quant_int8(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t m,
+                             const int8_t* signs, const float* block, int32_t group,
+                             int8_t* codes, void* scales, int32_t scale_dtype, void* stream) {
+  return rotate_quant("hr_rotate_quant_int8", 8, x, x_dtype, rows, n, m, signs, block, group,
+                      reinterpret_cast<uint8_t*>(codes), scales, scale_dtype, stream);
 }
 
 int32_t hr_butterfly_coeffs(const float* angles, int32_t n, int32_t precondition, float* coeffs,
@@ -207,10 +223,11 @@ int32_t hr_dequant_int4(const uint8_t* codes, const void* scales, int32_t scale_
                                      static_cast<hipStream_t>(stream)), fn);
 }
 
-int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales, const uint8_t* w_codes,
-                     const void* w_scales, int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
-                     int32_t group, float* c, int32_t* group_acc, void* stream) {
-  const char* fn = "hr_w4a4_gemm";
+// Shared body of hr_w4a4_gemm and hr_w4a8_gemm.
+static int32_t gemm(const char* fn, int a_int8, const uint8_t* a_codes, const void* a_scales,
+                    const uint8_t* w_codes, const void* w_scales, int32_t scale_dtype, int64_t M,
+                    int64_t N, int64_t K, int32_t group, float* c, int32_t* group_acc,
+                    void* stream) {
   if (M < 0 || N < 0 || K < 0) return fail(HR_EINVAL, "%s: negative size", fn);
   if (M > 0 && N > 0 && (!a_codes || !a_scales || !w_codes || !w_scales || !c))
     return fail(HR_EINVAL, "%s: a_codes, a_scales, w_codes, w_scales and c are required", fn);
@@ -228,6 +245,7 @@ int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales, const uint8_t
   if (M == 0 || N == 0) return ok();
   hr::GemmArgs a{};
   a.a = a_codes;
+  a.a_int8 = a_int8;
   a.sa = a_scales;
   a.w = w_codes;
   a.sw = w_scales;
@@ -239,6 +257,20 @@ int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales, const uint8_t
   a.c = c;
   a.group_acc = group_acc;
   return from_hip(hr::launch_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales, const uint8_t* w_codes,
+                     const void* w_scales, int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
+                     int32_t group, float* c, int32_t* group_acc, void* stream) {
+  return gemm("hr_w4a4_gemm", 0, a_codes, a_scales, w_codes, w_scales, scale_dtype, M, N, K, group,
+              c, group_acc, stream);
+}
+
+int32_t hr_w4a8_gemm(const int8_t* a_codes, const void* a_scales, const uint8_t* w_codes,
+                     const void* w_scales, int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
+                     int32_t group, float* c, int32_t* group_acc, void* stream) {
+  return gemm("hr_w4a8_gemm", 1, reinterpret_cast<const uint8_t*>(a_codes), a_scales, w_codes,
+              w_scales, scale_dtype, M, N, K, group, c, group_acc, stream);
 }
 
 }  // extern "C"

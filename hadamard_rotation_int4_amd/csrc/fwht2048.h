@@ -126,13 +126,18 @@ __device__ __forceinline__ uint32_t umax_dpp(uint32_t a) {
   return a > b ? a : b;
 }
 
-// Correctly rounded fp32 a / 7 (one residual correction of a * RN(1/7)).
-__device__ __forceinline__ float div7(float a) {
-  const float r7 = 1.0f / 7.0f;
-  const float q0 = a * r7;
-  const float r = fmaf(-q0, 7.0f, a);
-  return fmaf(r, r7, q0);
+// Correctly rounded fp32 a / D for D = 7 and D = 127 (one residual
+// correction of a * RN(1/D); checked against IEEE division over every
+// mantissa at several exponents and over all subnormal inputs).
+template <int D>
+__device__ __forceinline__ float div_const(float a) {
+  static_assert(D == 7 || D == 127, "checked divisors only");
+  const float rd = 1.0f / (float)D;
+  const float q0 = a * rd;
+  const float r = fmaf(-q0, (float)D, a);
+  return fmaf(r, rd, q0);
 }
+__device__ __forceinline__ float div7(float a) { return div_const<7>(a); }
 
 // Pack 8 codes held as magic-rounded floats (bits = 0x4B400008 + q, so the
 // low byte is q + 8 in [1, 15] with clean high nibble) into one dword of

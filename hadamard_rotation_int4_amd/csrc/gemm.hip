@@ -7,7 +7,8 @@
 // submission per group).
 //
 // Straightforward tile kernel: a 64x64 output tile per workgroup of 4 waves,
-// one K group per iteration: packed codes are unpacked to int8 in LDS, each
+// one K group per iteration: packed codes are unpacked to int8 in LDS (int8
+// activation codes of W4A8 are copied as they are), each
 // wave runs 2x2 v_mfma_i32_16x16x64_i8 tiles over the group, then converts the
 // group's int32 sums to fp32 and accumulates them with sA * sW.
 #include "hr_internal.h"
@@ -63,10 +64,17 @@ __global__ __launch_bounds__(256) void w4a4_gemm_simple_kernel(GemmArgs g) {
     for (int idx = tid; idx < kTile * words_per_row; idx += 256) {
       const int r = idx / words_per_row, c = idx % words_per_row;
       const int64_t kb = (int64_t)gi * (G / 2) + c * 4;  // byte offset in the packed row
-      uint32_t qa = 0, qw = 0;
-      if (m0 + r < g.M) qa = *reinterpret_cast<const uint32_t*>(g.a + (m0 + r) * (K / 2) + kb);
-      qw = *reinterpret_cast<const uint32_t*>(g.w + (n0 + r) * (K / 2) + kb);
-      *reinterpret_cast<uint64_t*>(la + r * G + c * 8) = unpack8(qa);
+      uint64_t a8 = 0;
+      if (g.a_int8) {
+        if (m0 + r < g.M)
+          a8 = *reinterpret_cast<const uint64_t*>(g.a + (m0 + r) * K + (int64_t)gi * G + c * 8);
+      } else {
+        uint32_t qa = 0;
+        if (m0 + r < g.M) qa = *reinterpret_cast<const uint32_t*>(g.a + (m0 + r) * (K / 2) + kb);
+        a8 = unpack8(qa);
+      }
+      const uint32_t qw = *reinterpret_cast<const uint32_t*>(g.w + (n0 + r) * (K / 2) + kb);
+      *reinterpret_cast<uint64_t*>(la + r * G + c * 8) = a8;
       *reinterpret_cast<uint64_t*>(lw + r * G + c * 8) = unpack8(qw);
     }
     __syncthreads();

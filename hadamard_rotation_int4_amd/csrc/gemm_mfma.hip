@@ -1,7 +1,8 @@
-// W4A4 GEMM on CDNA4 int8 MFMA, tiled kernels.
+// W4A4 and W4A8 GEMMs on CDNA4 int8 MFMA, tiled kernels.
 //
 // What is computed ("Experiment -- Hadamard rotation for int4 (W4A4)
-// accuracy", Hypothesis and Verdict): C = A W^T with
+// accuracy", Hypothesis and Verdict; W4A8 is the same page's act8/wt4 rows of
+// Results): C = A W^T with
 //   acc[m][n][g] = sum_{k in group g} a[m][k] w[n][k]   (exact int32)
 //   C[m][n]      = sum_g sA[m][g] sW[n][g] acc[m][n][g]  (fp32)
 //
@@ -9,7 +10,10 @@
 // nibble.  x & 0xF0F0F0F0 turns a dword of 8 codes into 4 int8 bytes equal to
 // 16 * (odd codes), (x << 4) & 0xF0F0F0F0 into 16 * (even codes).  Both
 // operands get the same K permutation, so every int32 sum is exactly 256 times
-// the true group sum; the 1/256 is applied (exactly) to the fp32 result.
+// the true group sum; the 1/256 is applied (exactly) to the fp32 result.  In
+// W4A8 the activations are int8 codes already: v_perm_b32 puts their bytes in
+// the order the weight unpack produces (k = 0 2 4 6 | 1 3 5 7 per 8 codes),
+// and the sums are 16 times the true ones.
 //
 // Prefill kernel (M > 16): a 128x128 output tile per workgroup of 4 waves,
 // 64x64 per wave as 2x2 v_mfma_i32_32x32x32_i8 tiles, stages of up to 128
@@ -30,6 +34,17 @@
 namespace hr {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+// 16 int8 codes in natural order -> the K order of unpack16 (k = 0 2 4 6,
+// 1 3 5 7, 8 10 12 14, 9 11 13 15)
+__device__ __forceinline__ v4i order_int8(uint4 p) {
+  v4i r;
+  r.x = (int)__builtin_amdgcn_perm(p.y, p.x, 0x06040200u);
+  r.y = (int)__builtin_amdgcn_perm(p.y, p.x, 0x07050301u);
+  r.z = (int)__builtin_amdgcn_perm(p.w, p.z, 0x06040200u);
+  r.w = (int)__builtin_amdgcn_perm(p.w, p.z, 0x07050301u);
+  return r;
+}
 
 __device__ __forceinline__ v4i unpack16(uint2 p) {
   v4i r;
@@ -98,14 +113,16 @@ constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100, kSchedDs
 // ring, so the lower tiles can still read the previous group's scales after
 // other waves have stored the next stage's.  Stages are unrolled in pairs so
 // that the LDS buffer of every access is a compile-time offset.
-template <int G, bool F16, bool WRITE_ACC>
+template <int G, bool F16, bool WRITE_ACC, bool A8>
 __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
   constexpr int KS = G < 128 ? G : 128;   // codes per pipeline stage
   constexpr int STEPS = KS / 32;          // MFMA K-steps per stage
   constexpr int SPG = G / KS;             // stages per group (1 or 2)
   constexpr int PPR = KS / 32;            // 16-byte packed pieces per row and stage
-  constexpr int LOADS = PPR;              // pieces per thread and stage (both operands)
-  constexpr int LPO = LOADS / 2;          // pieces per thread and operand
+  constexpr int PPA = A8 ? 2 * PPR : PPR; // 16-byte pieces per A row and stage
+  constexpr int LPO = PPR / 2;            // W pieces per thread and stage
+  constexpr int LPA = PPA / 2;            // A pieces per thread and stage
+  constexpr int LOADS = LPA + LPO;
   constexpr int OPB = (KS / 16) * 128 * 16;   // bytes of one operand stage in LDS
   constexpr int LSC = 4 * OPB;            // byte offset of the scale ring
   constexpr int SB = F16 ? 2 : 4;         // bytes per scale
@@ -118,24 +135,30 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int64_t n0 = (int64_t)blockIdx.x * kBN;
   const int64_t rowb = g.K / 2;           // bytes per packed row
+  const int64_t rowb_a = A8 ? g.K : rowb; // bytes per A row
   const int ngroups = (int)(g.K / G);
   const int nstages = (int)(g.K / KS);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
 
-  // Packed operand panels and this thread's pieces: piece t of operand op is
-  // tile row srow + t' * 256 / PPR (t' = t mod LPO), 16-byte piece spc; A rows
-  // past M read row 0 of the panel instead (a valid address; never stored).
+  // Operand panels and this thread's pieces: A piece t < LPA is tile row
+  // srow_a + t * 256 / PPA, 16-byte piece spc_a; W piece LPA + t is row
+  // srow + t * 256 / PPR, piece spc.  A rows past M read row 0 of the panel
+  // instead (a valid address; never stored).
   const __amdgpu_buffer_rsrc_t rs_a =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(g.a + m0 * rowb), 0, (int)(128 * rowb), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(g.a + m0 * rowb_a), 0, (int)(128 * rowb_a), 0x00020000);
   const __amdgpu_buffer_rsrc_t rs_w =
       __builtin_amdgcn_make_buffer_rsrc((void*)(g.w + n0 * rowb), 0, (int)(128 * rowb), 0x00020000);
   const int srow = tid / PPR, spc = tid % PPR;
+  const int srow_a = tid / PPA, spc_a = tid % PPA;
   int voff[LOADS];
 #pragma unroll
   for (int t = 0; t < LOADS; ++t) {
-    const int r = srow + (t % LPO) * (256 / PPR);
-    const bool clamp = t < LPO && m0 + r >= g.M;
-    voff[t] = (clamp ? 0 : r) * (int)rowb + 16 * spc;
+    if (t < LPA) {
+      const int r = srow_a + t * (256 / PPA);
+      voff[t] = (m0 + r >= g.M ? 0 : r) * (int)rowb_a + 16 * spc_a;
+    } else {
+      voff[t] = (srow + (t - LPA) * (256 / PPR)) * (int)rowb + 16 * spc;
+    }
   }
   // scale row of this thread: threads 0-127 (waves 0, 1) A rows, 128-255 W rows
   const int64_t sr = tid < kBM ? (m0 + tid < g.M ? m0 + tid : m0) : n0 + tid - kBM;
@@ -145,12 +168,17 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
 
   // LDS byte offsets: this thread's store slot (chunk 2 spc, row srow), and
   // the fragment read slots of K-step ks (chunk 2 ks + h, row wm + l32 or
-  // wn + l32) within an operand stage
+  // wn + l32) within an operand stage.  int8 A pieces are one chunk each
+  // (chunk spc_a); their rows are XORed with spc_a * 16 / PPA, which keeps
+  // the 8- and 16-lane store phases (one or two rows, PPA chunks) and the
+  // read phases free of bank conflicts.
   const int st_off = (2 * spc * 128 + (srow ^ row_xor<PPR>(spc))) * 16;
+  const int st_off_a = (spc_a * 128 + (srow_a ^ (spc_a * (16 / PPA)))) * 16;
   int rd_a[STEPS], rd_b[STEPS];
 #pragma unroll
   for (int ks = 0; ks < STEPS; ++ks) {
-    rd_a[ks] = (h * 128 + wm + (l32 ^ row_xor<PPR>(ks))) * 16;
+    const int xa = A8 ? (2 * ks + h) * (16 / PPA) : row_xor<PPR>(ks);
+    rd_a[ks] = (h * 128 + wm + (l32 ^ xa)) * 16;
     rd_b[ks] = OPB + (h * 128 + wn + (l32 ^ row_xor<PPR>(ks))) * 16;
   }
 
@@ -168,10 +196,11 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
   v4u pre[LOADS];
   uint32_t psc = 0;
   auto load_stage = [&](int s) {
-    const int so = s * (KS / 2);
+    const int so = s * (KS / 2), so_a = A8 ? s * KS : so;
 #pragma unroll
     for (int t = 0; t < LOADS; ++t)
-      pre[t] = __builtin_amdgcn_raw_buffer_load_b128(t < LPO ? rs_a : rs_w, voff[t], so, 0);
+      pre[t] = __builtin_amdgcn_raw_buffer_load_b128(t < LPA ? rs_a : rs_w, voff[t],
+                                                     t < LPA ? so_a : so, 0);
     const int gso = (s / SPG) * SB;
     psc = F16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs_s, svoff, gso, 0)
               : __builtin_amdgcn_raw_buffer_load_b32(rs_s, svoff, gso, 0);
@@ -180,7 +209,13 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
     char* sb = smem + decltype(bufc)::value * 2 * OPB;
 #pragma unroll
     for (int t = 0; t < LOADS; ++t) {
-      char* d = sb + (t / LPO) * OPB + (t % LPO) * (256 / PPR) * 16 + st_off;
+      if (A8 && t < LPA) {
+        char* d = sb + t * (256 / PPA) * 16 + st_off_a;
+        *reinterpret_cast<v4i*>(d) = order_int8(make_uint4(pre[t].x, pre[t].y, pre[t].z, pre[t].w));
+        continue;
+      }
+      const int op = t < LPA ? 0 : 1, tt = t < LPA ? t : t - LPA;
+      char* d = sb + op * OPB + tt * (256 / PPR) * 16 + st_off;
       *reinterpret_cast<v4i*>(d) = unpack16(make_uint2(pre[t].x, pre[t].y));
       *reinterpret_cast<v4i*>(d + 2048) = unpack16(make_uint2(pre[t].z, pre[t].w));
     }
@@ -246,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
         for (int v = 0; v < 16; ++v) {
           const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
           const int64_t col = n0 + wn + 32 * j + l32;
-          if (row < g.M) g.group_acc[(row * g.N + col) * ngroups + gi] = acc[i][j][v] >> 8;
+          if (row < g.M) g.group_acc[(row * g.N + col) * ngroups + gi] = acc[i][j][v] >> (A8 ? 4 : 8);
         }
     }
   };
@@ -302,7 +337,9 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
   if (s < nstages) stage(s, IntC<0>{});
   epilogue(1, (nstages - 1) % 3, ngroups - 1);
 
-  // every int32 sum is 256 times the true one (both operands carry 16 x code)
+  // every int32 sum is 256 (W4A8: 16) times the true one: each int4 operand
+  // carries 16 x code
+  constexpr float kUnscale = A8 ? 1.0f / 16.0f : 1.0f / 256.0f;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -310,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
       const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
       if (row < g.M) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) g.c[row * g.N + n0 + wn + 32 * j + l32] = c[i][j][v] * (1.0f / 256.0f);
+        for (int j = 0; j < 2; ++j) g.c[row * g.N + n0 + wn + 32 * j + l32] = c[i][j][v] * kUnscale;
       }
     }
 }
@@ -329,6 +366,11 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
 // slots for A and W, so group sums stay exact) with one ds_read_b64, and the
 // piece XOR spreads the 16 rows over all LDS banks.  The 16 partial 16 x 16
 // tiles are summed through LDS.
+//
+// W4A8: an A run is 128 bytes; two loads cover its 16 rows (lane l of load i
+// reads row 8 i + l / 8, piece (l % 8) ^ ((row / 2) % 8): eight lanes per 128
+// contiguous bytes), and lane (r, j) reads its 16 codes of half h as one
+// ds_read_b128 of piece 4 h + j, reordered with v_perm_b32.
 constexpr int kDecWaves = 16;
 constexpr int kDecRuns = 2;      // runs per operand and chunk
 
@@ -337,7 +379,7 @@ __device__ __forceinline__ void dec_lds_load16(const void* gp, void* lp) {
 }
 __device__ __forceinline__ void dec_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int G, bool F16, bool WRITE_ACC>
+template <int G, bool F16, bool WRITE_ACC, bool A8>
 __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmArgs g) {
   constexpr int CH = kDecRuns;
   constexpr int MPG = G / 64;                    // MFMAs per group
@@ -346,12 +388,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
   typedef typename std::conditional<F16, _Float16, float>::type scale_t;
   __shared__ float part[kDecWaves][16 * 16];
   __shared__ __attribute__((aligned(16))) float sat[kDecWaves][GPC][16];   // [group][A row]
-  __shared__ __attribute__((aligned(16))) uint4 stage[kDecWaves][2][CH][64];
+  __shared__ __attribute__((aligned(16))) uint4 stage_w[kDecWaves][CH][64];
+  __shared__ __attribute__((aligned(16))) uint4 stage_a4[A8 ? 1 : kDecWaves][CH][64];
+  __shared__ __attribute__((aligned(16))) uint4 stage_a8[A8 ? kDecWaves : 1][CH][128];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
   const int64_t rowb = g.K / 2;
+  const int64_t rowb_a = A8 ? g.K : rowb;
   const int ngroups = (int)(g.K / G);
   const int units = (int)(g.K / (128 * RPU));
   const int rbeg = RPU * (wave * units / kDecWaves), rend = RPU * ((wave + 1) * units / kDecWaves);
@@ -359,6 +404,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
   // loads: row l / 4, piece (l % 4) ^ ((l / 16) % 4)
   const int lrow = lane >> 2, lpiece = (lane & 3) ^ ((lane >> 4) & 3);
   const uint8_t* la = g.a + (int64_t)(lrow < g.M ? lrow : 0) * rowb + 16 * lpiece;
+  // int8 A: load i reads row 8 i + l / 8, piece (l % 8) ^ ((row / 2) % 8)
+  const int arow0 = lane >> 3, arow1 = 8 + (lane >> 3);
+  const uint8_t* la8_0 = g.a + (int64_t)(arow0 < g.M ? arow0 : 0) * rowb_a +
+                         16 * ((lane & 7) ^ ((arow0 >> 1) & 7));
+  const uint8_t* la8_1 = g.a + (int64_t)(arow1 < g.M ? arow1 : 0) * rowb_a +
+                         16 * ((lane & 7) ^ ((arow1 >> 1) & 7));
+  const uint32_t rd8 = 16u * (uint32_t)(8 * r);   // + 16 * ((4 h + j) ^ ((r / 2) % 8))
   const uint8_t* lw = g.w + (n0 + lrow) * rowb + 16 * lpiece;
   // reads, half h of a run: piece 2 h + j / 2, byte 8 (j % 2) of it
   const uint32_t rd0 = 64 * r + 16 * ((0 + (j >> 1)) ^ ((r >> 2) & 3)) + 8 * (j & 1);
@@ -380,9 +432,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
     }
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
-      const int64_t off = (int64_t)(r0 + (t < nr ? t : nr - 1)) * 64;
-      dec_lds_load16(la + off, &stage[wave][0][t][0]);
-      dec_lds_load16(lw + off, &stage[wave][1][t][0]);
+      const int64_t run = r0 + (t < nr ? t : nr - 1);
+      if (A8) {
+        dec_lds_load16(la8_0 + run * 128, &stage_a8[wave][t][0]);
+        dec_lds_load16(la8_1 + run * 128, &stage_a8[wave][t][64]);
+      } else {
+        dec_lds_load16(la + run * 64, &stage_a4[wave][t][0]);
+      }
+      dec_lds_load16(lw + run * 64, &stage_w[wave][t][0]);
     }
     dec_wait_loads();
     // A scales transposed through this wave's LDS: lane reads rows 4 j .. 4 j + 3
@@ -392,8 +449,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
         if (u < ng) sat[wave][u][r] = arow ? (float)sab[u] : 0.0f;
     }
     __builtin_amdgcn_wave_barrier();
-    const char* sta = reinterpret_cast<const char*>(&stage[wave][0][0][0]);
-    const char* stw = reinterpret_cast<const char*>(&stage[wave][1][0][0]);
+    const char* sta = reinterpret_cast<const char*>(&stage_a4[A8 ? 0 : wave][0][0]);
+    const char* stw = reinterpret_cast<const char*>(&stage_w[wave][0][0]);
 #pragma unroll
     for (int u = 0; u < GPC; ++u) {
       if (u >= ng) break;
@@ -401,13 +458,21 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
 #pragma unroll
       for (int m = u * MPG; m < (u + 1) * MPG; ++m) {
         const uint32_t o = 1024u * (m >> 1) + ((m & 1) ? rd1 : rd0);
-        const uint2 pa = *reinterpret_cast<const uint2*>(sta + o);
         const uint2 pw = *reinterpret_cast<const uint2*>(stw + o);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-            unpack16(make_uint2(arow ? pa.x : 0u, arow ? pa.y : 0u)), unpack16(pw), acc, 0, 0, 0);
+        v4i av;
+        if (A8) {
+          const int pc = (4 * (m & 1) + j) ^ ((r >> 1) & 7);
+          const uint4 pa = *reinterpret_cast<const uint4*>(
+              reinterpret_cast<const char*>(&stage_a8[wave][m >> 1][0]) + rd8 + 16 * pc);
+          av = arow ? order_int8(pa) : (v4i){0, 0, 0, 0};
+        } else {
+          const uint2 pa = *reinterpret_cast<const uint2*>(sta + o);
+          av = unpack16(make_uint2(arow ? pa.x : 0u, arow ? pa.y : 0u));
+        }
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, unpack16(pw), acc, 0, 0, 0);
       }
       // lane holds rows 4 j + v of column n0 + r
-      const float sw = (float)swb[u] * (1.0f / 256.0f);
+      const float sw = (float)swb[u] * (A8 ? 1.0f / 16.0f : 1.0f / 256.0f);
       const float4 s4 = *reinterpret_cast<const float4*>(&sat[wave][u][4 * j]);
       const float sar[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
@@ -416,7 +481,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
         if (WRITE_ACC) {
           const int row = 4 * j + v;
           if (row < g.M)
-            g.group_acc[((int64_t)row * g.N + n0 + r) * ngroups + g0 + u] = acc[v] >> 8;
+            g.group_acc[((int64_t)row * g.N + n0 + r) * ngroups + g0 + u] = acc[v] >> (A8 ? 4 : 8);
         }
       }
     }
@@ -436,24 +501,29 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
   }
 }
 
-template <int G, bool F16, bool WRITE_ACC>
+template <int G, bool F16, bool WRITE_ACC, bool A8>
 static void launch_g(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 16) {
-    hipLaunchKernelGGL((w4a4_gemm_decode_kernel<G, F16, WRITE_ACC>), dim3((unsigned)(a.N / 16)),
+    hipLaunchKernelGGL((w4a4_gemm_decode_kernel<G, F16, WRITE_ACC, A8>), dim3((unsigned)(a.N / 16)),
                        dim3(kDecWaves * 64), 0, s, a);
   } else {
     const dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM));
-    hipLaunchKernelGGL((w4a4_gemm_tile_kernel<G, F16, WRITE_ACC>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((w4a4_gemm_tile_kernel<G, F16, WRITE_ACC, A8>), grid, dim3(256), 0, s, a);
+  }
+}
+
+template <int G, bool A8>
+static void launch_dt(const GemmArgs& a, hipStream_t s) {
+  if (a.scale_f16) {
+    if (a.group_acc) launch_g<G, true, true, A8>(a, s); else launch_g<G, true, false, A8>(a, s);
+  } else {
+    if (a.group_acc) launch_g<G, false, true, A8>(a, s); else launch_g<G, false, false, A8>(a, s);
   }
 }
 
 template <int G>
-static void launch_dt(const GemmArgs& a, hipStream_t s) {
-  if (a.scale_f16) {
-    if (a.group_acc) launch_g<G, true, true>(a, s); else launch_g<G, true, false>(a, s);
-  } else {
-    if (a.group_acc) launch_g<G, false, true>(a, s); else launch_g<G, false, false>(a, s);
-  }
+static void launch_da(const GemmArgs& a, hipStream_t s) {
+  if (a.a_int8) launch_dt<G, true>(a, s); else launch_dt<G, false>(a, s);
 }
 
 // The prefill kernel needs N % 128 == 0; the decode kernel takes every shape
@@ -463,9 +533,9 @@ bool launch_gemm_mfma(const GemmArgs& a, hipStream_t s) {
   const bool decode = a.M <= 16;
   if (!decode && a.N % kBN) return false;
   switch (a.group) {
-    case 64: launch_dt<64>(a, s); return true;
-    case 128: launch_dt<128>(a, s); return true;
-    case 256: launch_dt<256>(a, s); return true;
+    case 64: launch_da<64>(a, s); return true;
+    case 128: launch_da<128>(a, s); return true;
+    case 256: launch_da<256>(a, s); return true;
     default: return false;
   }
 }

@@ -35,11 +35,11 @@ __device__ __forceinline__ float store_scale(void* scales, int64_t idx, float s3
 
 // Reference-style code of one value: round half away from zero, clamp to +-7,
 // zero for a zero scale.  Used by the straightforward kernels.
-__device__ __forceinline__ int quant_code_exact(float y, float s) {
+__device__ __forceinline__ int quant_code_exact(float y, float s, float qmax = 7.0f) {
   if (s == 0.0f) return 0;
   float t = y / s;                       // IEEE division
   float a = floorf(fabsf(t) + 0.5f);     // exact for |t| < 2^22
-  a = fminf(a, 7.0f);
+  a = fminf(a, qmax);
   int q = (int)a;
   return t < 0.0f ? -q : q;
 }

@@ -17,7 +17,8 @@ struct RhtArgs {
   const float* block;    // [m][m], null when m == 1
   float* y;              // fp32 output or null
   int group;             // quantization group (when codes != null)
-  uint8_t* codes;        // packed int4 output or null
+  uint8_t* codes;        // packed int4 (bits 4) or int8 (bits 8) codes, or null
+  int bits;              // 4 or 8 (when codes != null)
   void* scales;          // scale output or null
   int scale_f16;         // 1: fp16 scales, 0: fp32 scales
 };
@@ -38,7 +39,8 @@ struct ButterflyArgs {
 };
 
 struct GemmArgs {
-  const uint8_t* a;
+  const uint8_t* a;      // packed int4 [M][K/2], or int8 [M][K] when a_int8
+  int a_int8;            // 1: W4A8 (int8 activation codes)
   const void* sa;
   const uint8_t* w;
   const void* sw;

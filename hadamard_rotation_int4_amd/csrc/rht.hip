@@ -69,8 +69,9 @@ __global__ __launch_bounds__(kGenericThreads) void rht_generic_kernel(RhtArgs a,
       for (int i = tid; i < n; i += kGenericThreads) yr[i] = sm[i] * norm;
     }
     if (a.codes) {
-      quant_row_from_lds(sm, norm, n, a.group, a.codes + row * (n >> 1), a.scales,
-                         row * (n / a.group), a.scale_f16);
+      const int64_t row_bytes = a.bits == 8 ? n : (n >> 1);
+      quant_row_from_lds(sm, norm, n, a.group, a.codes + row * row_bytes, a.scales,
+                         row * (n / a.group), a.scale_f16, a.bits);
     }
     __syncthreads();
   }

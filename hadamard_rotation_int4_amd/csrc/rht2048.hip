@@ -183,6 +183,7 @@ static bool dispatch_in(const RhtArgs& a, float norm, hipStream_t s) {
 // quantization.  Returns false when the case belongs to the general kernel.
 bool launch_rht2048(const RhtArgs& a, hipStream_t s) {
   if (a.p != 2048 || a.m < 1 || a.m > 16) return false;
+  if (a.codes && a.bits == 8) return false;     // int8 codes: generic kernel
   if (a.m > 1 && (size_t)a.m * 2048 * sizeof(float) > 160 * 1024) return false;
   const float norm = (float)(1.0 / sqrt(2048.0));
   return a.x_bf16 ? dispatch_in<true>(a, norm, s) : dispatch_in<false>(a, norm, s);

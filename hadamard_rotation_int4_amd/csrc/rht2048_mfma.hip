@@ -1,12 +1,13 @@
 // Randomized Hadamard transform of bf16 rows of 2048 elements, fused with
-// int4 quantization (or an fp32 store), with the 128-point factor of the
-// transform on bf16 matrix cores.
+// int4 or int8 quantization (or an fp32 store), with the 128-point factor of
+// the transform on bf16 matrix cores.
 //
 // What is computed: y = H_2048 (d * x) / sqrt(2048) per row, Sylvester order
 // ("Experiment -- Hadamard rotation for int4 (W4A4) accuracy", Hypothesis and
 // Method; "Llama-3.2-1B-Instruct-HadamardSpin-4bits", How it Works), then
 // groups of G consecutive outputs quantized with scale absmax / 7 (same
-// pages, Method).
+// pages, Method); or, for the int8 activations of W4A8, with scale absmax / 127
+// (same page, the W4A8 rows of Results).
 //
 // The transform is the matrix-core routine of mfma2048.h (H_128 on
 // v_mfma_f32_16x16x32_bf16, H_16 as DPP butterflies).
@@ -18,15 +19,15 @@
 //     runs and the 16 pieces a lane group needs for one MFMA are consecutive
 //     LDS slots (no bank conflicts).
 //   Codes: a lane owns four runs of 8 consecutive outputs; they are staged
-//     through LDS (swizzled, conflict-free) and written as one contiguous
-//     1 KB row per store instruction.
+//     through LDS (swizzled, conflict-free) and written as contiguous 1 KB
+//     runs, one per store instruction (one per int4 row, two per int8 row).
 #include "mfma2048.h"
 
 namespace hr {
 
 constexpr int kMfmaBlocksPerCu = 2;
 
-template <int G, bool SCALE_F16, bool OUT_F32>
+template <int G, bool SCALE_F16, bool OUT_F32, int BITS>
 __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ signs, int64_t rows,
     float* __restrict__ yout, uint8_t* __restrict__ codes, void* __restrict__ scales, float norm) {
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
 
   // LDS of this wave: two row stages (256 slots of 16 bytes) and one row of codes
   __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][2][256];
-  __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][64];
+  __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][BITS == 8 ? 128 : 64];
   // element offset of this lane's piece within a row, per load j: + 32 j
   const int lane_src = 128 * (lane & 15) + 8 * (lane >> 4);
   auto issue = [&](int64_t row, int st) {
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
     bool need_clamp = false;
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const float s32 = div7(mg[i] * norm);
+      const float s32 = div_const<BITS == 8 ? 127 : 7>(mg[i] * norm);
       const float s = SCALE_F16 ? (float)(_Float16)s32 : s32;
       kk[i] = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s) * tau : 0.0f;
       need_clamp |= s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
@@ -134,7 +135,9 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
       }
     }
     const bool clamp = __builtin_amdgcn_ballot_w64(need_clamp) != 0;
-    const float M = 12582920.0f;                 // 1.5 * 2^23 + 8
+    // q + M rounds y k to an integer in the low mantissa bits (ties to even)
+    constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
+    const float M = BITS == 8 ? 12582912.0f : 12582920.0f;   // 1.5 * 2^23 (+ 8 for nibbles)
     u32x4* cl = &code_lds[wib][0];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -144,15 +147,39 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
                      fmaf(hi[0], k, M), fmaf(hi[1], k, M), fmaf(hi[2], k, M), fmaf(hi[3], k, M)};
       if (clamp) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rr[e] = __builtin_amdgcn_fmed3f(rr[e], M - 7.0f, M + 7.0f);
+        for (int e = 0; e < 8; ++e) rr[e] = __builtin_amdgcn_fmed3f(rr[e], M - QMAX, M + QMAX);
       }
-      // dword 16 a + 4 m + g of the row: 16-byte block (a, m) at 4 a + (m ^ (a >> 2 & 3))
-      reinterpret_cast<uint32_t*>(cl)[4 * (4 * a4 + (m ^ ((a4 >> 2) & 3))) + g] = pack8(rr);
+      if (BITS == 4) {
+        // dword 16 a + 4 m + g of the row: 16-byte block (a, m) at 4 a + (m ^ (a >> 2 & 3))
+        reinterpret_cast<uint32_t*>(cl)[4 * (4 * a4 + (m ^ ((a4 >> 2) & 3))) + g] = pack8(rr);
+      } else {
+        // the low byte of each float is its two's-complement code
+        uint32_t u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = __float_as_uint(rr[e]);
+        const uint32_t d0 = (__builtin_amdgcn_perm(u[3], u[2], 0x0c0c0400u) << 16) |
+                            __builtin_amdgcn_perm(u[1], u[0], 0x0c0c0400u);
+        const uint32_t d1 = (__builtin_amdgcn_perm(u[7], u[6], 0x0c0c0400u) << 16) |
+                            __builtin_amdgcn_perm(u[5], u[4], 0x0c0c0400u);
+        // 8-byte slot 16 a + 4 m + g of the row, its low 4 bits XOR 2 (a >> 1):
+        // the 32 lanes of a write phase hit 32 different bank pairs
+        reinterpret_cast<uint2*>(cl)[16 * a4 + ((4 * m + g) ^ (2 * (a4 >> 1)))] = make_uint2(d0, d1);
+      }
     }
-    // lane i stores bytes 16 i .. 16 i + 15 of the row: block (i >> 2, i & 3)
-    const int ra = lane >> 2, rm = lane & 3;
-    const u32x4 out = cl[4 * ra + (rm ^ ((ra >> 2) & 3))];
-    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * (N / 2)) + lane);
+    if (BITS == 4) {
+      // lane i stores bytes 16 i .. 16 i + 15 of the row: block (i >> 2, i & 3)
+      const int ra = lane >> 2, rm = lane & 3;
+      const u32x4 out = cl[4 * ra + (rm ^ ((ra >> 2) & 3))];
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * (N / 2)) + lane);
+    } else {
+      // 16-byte block b = 8 a + k of the row sits at 8 a + (k ^ (a >> 1))
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int b = 64 * h + lane, ra = b >> 3;
+        const u32x4 out = cl[8 * ra + ((b & 7) ^ (ra >> 1))];
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * N) + b);
+      }
+    }
   };
 
   int64_t row = wave;
@@ -166,17 +193,18 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
   }
 }
 
-template <int G, bool SCALE_F16, bool OUT_F32>
+template <int G, bool SCALE_F16, bool OUT_F32, int BITS = 4>
 static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
   int64_t blocks = (a.rows + 3) / 4;              // 4 waves per block, one row per wave
   const int64_t cap = 256 * kMfmaBlocksPerCu;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32>), dim3((unsigned)blocks), dim3(256),
+  hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS>), dim3((unsigned)blocks), dim3(256),
                      0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
                      a.scales, norm);
 }
 
-// bf16 rows of n = 2048 (m = 1): fp32 output or fused quantization.  Returns
+// bf16 rows of n = 2048 (m = 1): fp32 output or fused int4 / int8
+// quantization.  Returns
 // false when the case belongs to another kernel.
 bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s) {
   if (!a.x_bf16 || a.p != 2048 || a.m != 1) return false;
@@ -186,10 +214,15 @@ bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s) {
     return true;
   }
   if (!a.codes || a.y) return false;
-#define HR_MQ(G)                                                   \
-  case G:                                                          \
-    if (a.scale_f16) launch_mfma<G, true, false>(a, norm, s);      \
-    else launch_mfma<G, false, false>(a, norm, s);                 \
+#define HR_MQ(G)                                                             \
+  case G:                                                                    \
+    if (a.bits == 8) {                                                       \
+      if (a.scale_f16) launch_mfma<G, true, false, 8>(a, norm, s);           \
+      else launch_mfma<G, false, false, 8>(a, norm, s);                      \
+    } else {                                                                 \
+      if (a.scale_f16) launch_mfma<G, true, false>(a, norm, s);              \
+      else launch_mfma<G, false, false>(a, norm, s);                         \
+    }                                                                        \
     return true;
   switch (a.group) {
     HR_MQ(32)

@@ -1,7 +1,7 @@
 /*
- * hr.h -- C ABI of libhr.so: randomized Hadamard rotation, fused int4
- * quantization, HARP-style butterfly, int4 dequant and the W4A4 GEMM on
- * AMD Instinct MI355X (gfx950).
+ * hr.h -- C ABI of libhr.so: randomized Hadamard rotation, fused int4 (and
+ * int8) quantization, HARP-style butterfly, int4 dequant and the W4A4 (and
+ * W4A8) GEMM on AMD Instinct MI355X (gfx950).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -54,7 +54,7 @@ typedef enum {
 } hr_dtype;
 
 /* ABI version of this header (bumped on any signature change). */
-#define HR_ABI_VERSION 1
+#define HR_ABI_VERSION 2
 int32_t hr_abi_version(void);
 
 /* Static description of a status code. */
@@ -119,6 +119,30 @@ int32_t hr_rotate(const void* x, int32_t x_dtype, float* y, int64_t rows,
 int32_t hr_rotate_quant_int4(const void* x, int32_t x_dtype, int64_t rows,
                              int32_t n, int32_t m, const int8_t* signs,
                              const float* block, int32_t group, uint8_t* codes,
+                             void* scales, int32_t scale_dtype, void* stream);
+
+/*
+ * hr_rotate_quant_int8 -- hr_rotate fused with per-group symmetric absmax int8
+ * quantization: the activation operand of the W4A8 GEMM.
+ *
+ * Defines: as hr_rotate_quant_int4, with the 8-bit case of the experiment
+ * page's quantizer (Method: per-group symmetric quantization at any bit
+ * width) that its W4A8 (act8/wt4) rows of Results use for the activations.
+ *
+ * For every row and every group of G consecutive rotated values y:
+ *   a   = max |y| over the group           (fp32)
+ *   s32 = a / 127                           (fp32, correctly rounded)
+ *   s   = s32 rounded to fp16 (scale_dtype HR_F16) or s32 (HR_F32); stored
+ *   q   = y / s rounded to nearest, clamped to [-127, 127]; 0 when s == 0.
+ * Ties are resolved as in hr_rotate_quant_int4.
+ *
+ *   codes   [rows][n] int8, one code per element.
+ *   scales  [rows][n/G] of scale_dtype (HR_F16 or HR_F32).
+ *   other arguments and errors as hr_rotate_quant_int4.
+ */
+int32_t hr_rotate_quant_int8(const void* x, int32_t x_dtype, int64_t rows,
+                             int32_t n, int32_t m, const int8_t* signs,
+                             const float* block, int32_t group, int8_t* codes,
                              void* scales, int32_t scale_dtype, void* stream);
 
 /*
@@ -217,6 +241,29 @@ int32_t hr_dequant_int4(const uint8_t* codes, const void* scales,
  * Codes equal to -8 are accepted and multiply exactly.
  */
 int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales,
+                     const uint8_t* w_codes, const void* w_scales,
+                     int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
+                     int32_t group, float* c, int32_t* group_acc, void* stream);
+
+/*
+ * hr_w4a8_gemm -- C = A W^T with int8 activation codes and packed int4
+ * weights, per-group scales on both.
+ *
+ * Defines: "Experiment -- Hadamard rotation for int4 (W4A4) accuracy",
+ * Results (the W4A8 act8/wt4 rows: int8 activations against int4 weights)
+ * and the third of its conclusions (W4A8 is far more accurate than W4A4; an
+ * int8 MAC runs it directly); the sums and the scale fusion are those of
+ * hr_w4a4_gemm.
+ *
+ *   acc[m][n][g] = sum_{k = gG}^{gG+G-1} A[m][k] W[n][k]      (exact int32)
+ *   C[m][n]      = sum_g sA[m][g] sW[n][g] acc[m][n][g]       (fp32)
+ *
+ *   a_codes   [M][K] int8 (activations, K contiguous; hr_rotate_quant_int8
+ *             output).  Every int8 value is accepted.
+ *   w_codes   [N][K/2] uint8 packed int4 (weights).
+ *   other arguments, sizes and errors as hr_w4a4_gemm.
+ */
+int32_t hr_w4a8_gemm(const int8_t* a_codes, const void* a_scales,
                      const uint8_t* w_codes, const void* w_scales,
                      int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
                      int32_t group, float* c, int32_t* group_acc, void* stream);

@@ -38,22 +38,23 @@ def _f16_ambiguous(s32):
     return lo != hi
 
 
-def check_quant(codes_gpu, scales_gpu, y64, group, scale_mode="f16"):
-    """Compare packed codes and scales from the GPU against the oracle's
-    quantization of y64.  Returns a dict of counts for reporting."""
+def check_quant(codes_gpu, scales_gpu, y64, group, scale_mode="f16", bits=4):
+    """Compare codes (packed int4, or int8 when bits == 8) and scales from the
+    GPU against the oracle's quantization of y64.  Returns a dict of counts."""
     codes_gpu = np.asarray(codes_gpu)
     scales_gpu = np.asarray(scales_gpu)
     rows, n = y64.shape
     G = n // group
-    codes_o, scales_o, s_used_o = oracle.quant.quantize_groups(y64, group, scale_mode)
-    q_gpu = oracle.quant.unpack_int4(codes_gpu)
+    qmax = (1 << (bits - 1)) - 1
+    codes_o, scales_o, s_used_o = oracle.quant.quantize_groups(y64, group, scale_mode, bits)
+    q_gpu = oracle.quant.unpack_int4(codes_gpu) if bits == 4 else codes_gpu.view(np.int8)
     assert q_gpu.shape == codes_o.shape
     s_used = s_used_o.copy()
     n_amb = 0
     if scale_mode == "f16":
         assert scales_gpu.dtype == np.float16
         y32 = y64.astype(np.float32)
-        s32 = (np.abs(y32.reshape(rows, G, group)).max(-1) / np.float32(7)).astype(np.float32)
+        s32 = (np.abs(y32.reshape(rows, G, group)).max(-1) / np.float32(qmax)).astype(np.float32)
         amb = _f16_ambiguous(s32)
         eq = scales_gpu.view(np.uint16) == scales_o.view(np.uint16)
         bad = ~eq & ~amb
@@ -76,7 +77,7 @@ def check_quant(codes_gpu, scales_gpu, y64, group, scale_mode="f16"):
     # codes against the scale the GPU stored (identical to the oracle's except
     # in the exempt cases above)
     y32 = y64.astype(np.float32).reshape(rows, G, group)
-    ref = oracle.quant.codes_for_scale(y32, s_used, 7).reshape(rows, n)
+    ref = oracle.quant.codes_for_scale(y32, s_used, qmax).reshape(rows, n)
     t = oracle.quant.t_values(y64, s_used, group).astype(np.float64)
     frac = np.abs(t) - np.floor(np.abs(t))
     near_mid = np.abs(frac - 0.5) < MID_WIN

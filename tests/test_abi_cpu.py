@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert hr.lib.hr_abi_version() == 1
+    assert hr.lib.hr_abi_version() == 2
     for st in (hr.HR_OK, hr.HR_EINVAL, hr.HR_EUNSUPPORTED, hr.HR_EDEVICE):
         assert hr.lib.hr_status_string(st).startswith(b"HR_")
     assert b"unknown" in hr.lib.hr_status_string(99)
@@ -73,12 +73,12 @@ def test_rotate_zero_rows_is_noop():
     assert _rot(rows=0) == hr.HR_OK
 
 
-def _rq(**kw):
+def _rq(fn="hr_rotate_quant_int4", **kw):
     a = dict(x=P, dt=hr.HR_BF16, rows=4, n=2048, m=1, signs=None, block=None, group=128,
              codes=P, scales=P, sdt=hr.HR_F16)
     a.update(kw)
-    return hr.lib.hr_rotate_quant_int4(a["x"], a["dt"], a["rows"], a["n"], a["m"], a["signs"],
-                                       a["block"], a["group"], a["codes"], a["scales"], a["sdt"], None)
+    return getattr(hr.lib, fn)(a["x"], a["dt"], a["rows"], a["n"], a["m"], a["signs"],
+                               a["block"], a["group"], a["codes"], a["scales"], a["sdt"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -92,12 +92,15 @@ def _rq(**kw):
     (dict(codes=P + 1), hr.HR_EINVAL),
     (dict(signs=P + 2), hr.HR_EINVAL),
 ])
-def test_rotate_quant_validation(kw, status):
-    assert _rq(**kw) == status
+@pytest.mark.parametrize("fn", ["hr_rotate_quant_int4", "hr_rotate_quant_int8"])
+def test_rotate_quant_validation(fn, kw, status):
+    assert _rq(fn, **kw) == status
+    assert fn.encode() in hr.lib.hr_last_error()
 
 
-def test_rotate_quant_zero_rows_is_noop():
-    assert _rq(rows=0) == hr.HR_OK
+@pytest.mark.parametrize("fn", ["hr_rotate_quant_int4", "hr_rotate_quant_int8"])
+def test_rotate_quant_zero_rows_is_noop(fn):
+    assert _rq(fn, rows=0) == hr.HR_OK
 
 
 def test_butterfly_validation():
@@ -129,8 +132,9 @@ def test_dequant_validation():
     assert f(P, P, hr.HR_F16, 0, 256, 128, P, None) == hr.HR_OK
 
 
-def test_gemm_validation():
-    f = hr.lib.hr_w4a4_gemm
+@pytest.mark.parametrize("fn", ["hr_w4a4_gemm", "hr_w4a8_gemm"])
+def test_gemm_validation(fn):
+    f = getattr(hr.lib, fn)
     # a, sa, w, sw, sdt, M, N, K, group, c, acc, stream
     assert f(None, P, P, P, hr.HR_F16, 16, 64, 256, 128, P, None, None) == hr.HR_EINVAL
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 256, 128, None, None, None) == hr.HR_EINVAL
