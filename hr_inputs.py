@@ -145,6 +145,43 @@ def butterfly_inputs(rows: int = 32768, n: int = 4096, seed: int = SEED_BUTTERFL
     return ButterflyInputs(x=x, angles=angles, perm=perm, n=n, rows=rows)
 
 
+SEED_HARP = 6
+
+
+@dataclass
+class HarpInputs:
+    x: np.ndarray          # fp32 [rows][d]
+    radices: tuple         # the mixed-radix schedule, prod = d
+    theta: np.ndarray      # fp32, per stage [d / b][P_b] concatenated (P_2 = 1, P_b = b(b-1)/2)
+    fallbacks: list        # fp32 [b][b] orthogonal matrices, one per radix that is not a power of two
+    d: int
+    rows: int
+
+
+def harp_inputs(rows: int = 4096, radices=(8, 8, 8, 5, 2), seed: int = SEED_HARP,
+                theta_scale: float = 0.3, outlier_scale: float = 20.0) -> HarpInputs:
+    """The HARP summary's 5120 = (8, 8, 8, 5, 2) schedule by default.
+    Draw order: values (N(0,1) rows with round(0.001 d) channels scaled),
+    then per stage its parameters (b = 2: angles U(0, 2 pi); b > 2: Cayley
+    parameters N(0, theta_scale^2)), then one QR fallback per radix that is
+    not a power of two, in stage order."""
+    rng = _rng(seed)
+    radices = tuple(int(b) for b in radices)
+    d = int(np.prod(radices))
+    x = gaussian_rows_with_outliers(rng, rows, d, outlier_count(d), outlier_scale)
+    parts = []
+    for b in radices:
+        nb = d // b
+        if b == 2:
+            parts.append(rng.uniform(0.0, 2.0 * math.pi, size=nb))
+        else:
+            parts.append(rng.normal(0.0, theta_scale, size=nb * (b * (b - 1) // 2)))
+    theta = np.concatenate(parts).astype(np.float32)
+    fallbacks = [random_orthogonal_f32(rng, b) for b in radices if b & (b - 1)]
+    return HarpInputs(x=np.ascontiguousarray(x, dtype=np.float32), radices=radices, theta=theta,
+                      fallbacks=fallbacks, d=d, rows=rows)
+
+
 # Two's-complement nibble patterns of the int4 codes -7..7 (pattern 0x8, i.e. -8,
 # is never used by the symmetric quantizer).
 _NIBBLES = np.array([0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 11, 12, 13, 14, 15], dtype=np.uint8)

@@ -23,7 +23,10 @@ Modules and the passages they follow:
   needs int4 activations; Verdict: per-group work must not be split).
 * ``probe``        -- the matmul RMS-error probe (Method; Results, synthetic
   table).
+* ``harp``         -- HARP's general processor: mixed-radix stages of dense
+  blocks Q(theta) G_b (Givens for b = 2, Cayley map for b > 2).  HARP
+  technical summary, sections 2.1-2.2.
 
 Readings of points the pages leave open are stated where they are used.
 """
-from . import hadamard, mixed_radix, butterfly, quant, gemm, probe  # noqa: F401
+from . import hadamard, mixed_radix, butterfly, quant, gemm, probe, harp  # noqa: F401
