@@ -263,6 +263,25 @@ def main(argv=None):
             "bytes": bbq}
         del xb, yb
 
+        # HARP general processor: 4096 rows of d = 5120 = (8, 8, 8, 5, 2)
+        hi = hr_inputs.harp_inputs()
+        fb = torch.from_numpy(np.concatenate([f.ravel() for f in hi.fallbacks])).to(dev)
+        hblk = hr.harp_blocks(hi.radices, torch.from_numpy(hi.theta).to(dev), fb)
+        hx = torch.from_numpy(hi.x).to(dev)
+        hy = torch.empty_like(hx)
+        tab = hblk.numel() * 4                 # the block table, read once
+        msh = _timed(lambda i: hr.harp_apply(hx, hi.radices, hblk, out=hy), max(5, args.steps // 2), 3)
+        bh = hi.rows * hi.d * 8 + tab
+        kernels["harp_f32_4096x5120_r88852"] = {"ms": msh, "GB/s": bh / msh / 1e6,
+                                                "frac_hbm": bh / msh / 1e6 / HBM_PEAK_GBS, "bytes": bh}
+        mshq = _timed(lambda i: hr.harp_apply(hx, hi.radices, hblk, want_y=False, group=128),
+                      max(5, args.steps // 2), 3)
+        bhq = hi.rows * (hi.d * 4 + hi.d // 2 + (hi.d // 128) * 2) + tab
+        kernels["harp_quant_f32_4096x5120_r88852_g128"] = {
+            "ms": mshq, "GB/s": bhq / mshq / 1e6, "frac_hbm": bhq / mshq / 1e6 / HBM_PEAK_GBS,
+            "bytes": bhq}
+        del hx, hy, hblk
+
         # W4A4 GEMM 4096^3 and M=16, G=128
         for M in (4096, 16):
             gi = hr_inputs.gemm_inputs(M=M)

@@ -5,8 +5,8 @@ W4A8 GEMMs on MI355X (gfx950).
 Argument marshalling only: every step runs in the library's HIP kernels on
 torch's current stream.  Tensors must be CUDA tensors, contiguous, of the
 dtypes stated per function; outputs are allocated with torch when not given.
-The library must be built in-tree first (``python -m
-hadamard_rotation_int4_amd.build``); importing without it raises ImportError.
+The library must be built in-tree first (``python
+hadamard_rotation_int4_amd/build.py``); importing without it raises ImportError.
 """
 from __future__ import annotations
 
@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = ["HRError", "rotate", "rotate_quant_int4", "rotate_quant_int8", "butterfly_coeffs",
-           "butterfly_apply", "dequant_int4", "w4a4_gemm", "w4a8_gemm", "lib", "LIB_PATH", "SYMBOLS",
+           "butterfly_apply", "harp_blocks", "harp_apply", "dequant_int4", "w4a4_gemm", "w4a8_gemm",
+           "lib", "LIB_PATH", "SYMBOLS",
            "HR_OK", "HR_EINVAL", "HR_EUNSUPPORTED", "HR_EDEVICE", "HR_F32", "HR_BF16", "HR_F16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhr.so")
@@ -36,6 +37,8 @@ SYMBOLS = {
     "hr_rotate_quant_int8": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
     "hr_butterfly_coeffs": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "hr_butterfly_apply": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "hr_harp_blocks": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp]),
+    "hr_harp_apply": (_i32, [_vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
     "hr_dequant_int4": (_i32, [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp]),
     "hr_w4a4_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "hr_w4a8_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
@@ -45,7 +48,7 @@ SYMBOLS = {
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m hadamard_rotation_int4_amd.build`")
+                          "`python hadamard_rotation_int4_amd/build.py`")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SYMBOLS.items():
         fn = getattr(handle, name)
@@ -173,6 +176,49 @@ def butterfly_apply(x: torch.Tensor, coeffs: torch.Tensor, precondition: bool = 
     _check(lib.hr_butterfly_apply(_ptr(x), _ptr(y), rows, n, _ptr(coeffs), int(precondition),
                                   _ptr(perm), int(inverse), g, _ptr(codes), _ptr(scales), sd,
                                   _stream(x.device)), "hr_butterfly_apply")
+    if group is None:
+        return y
+    return y, codes, scales
+
+
+def _radices(radices):
+    r = (ctypes.c_int32 * len(radices))(*[int(b) for b in radices])
+    return r, len(radices)
+
+
+def harp_blocks(radices, theta: torch.Tensor, fallbacks: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense blocks of a HARP schedule (hr_harp_blocks).  radices: a Python
+    sequence; theta: fp32 parameters; fallbacks: fp32 concatenated [b][b]
+    mixers of the radices that are not powers of two (or None)."""
+    arr, m = _radices(radices)
+    d = 1
+    for b in radices:
+        d *= int(b)
+    blocks = torch.empty(d * sum(int(b) for b in radices), dtype=torch.float32, device=theta.device)
+    _check(lib.hr_harp_blocks(arr, m, _ptr(theta), _ptr(fallbacks), _ptr(blocks),
+                              _stream(theta.device)), "hr_harp_blocks")
+    return blocks
+
+
+def harp_apply(x: torch.Tensor, radices, blocks: torch.Tensor, inverse: bool = False,
+               want_y: bool = True, group: int | None = None, scale_dtype=torch.float16,
+               out: torch.Tensor | None = None):
+    """The HARP processor (or its transpose) per row (hr_harp_apply).
+    Returns y, or (y_or_None, codes, scales) when ``group`` is given."""
+    rows, d = x.shape
+    arr, m = _radices(radices)
+    y = None
+    if want_y:
+        y = out if out is not None else torch.empty((rows, d), dtype=torch.float32, device=x.device)
+    codes = scales = None
+    g, sd = 0, HR_F16
+    if group is not None:
+        g = group
+        codes = torch.empty((rows, d // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((rows, d // group), dtype=scale_dtype, device=x.device)
+        sd = _dtype_code(scale_dtype)
+    _check(lib.hr_harp_apply(_ptr(x), _ptr(y), rows, arr, m, _ptr(blocks), int(inverse), g,
+                             _ptr(codes), _ptr(scales), sd, _stream(x.device)), "hr_harp_apply")
     if group is None:
         return y
     return y, codes, scales

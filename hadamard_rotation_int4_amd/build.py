@@ -1,6 +1,8 @@
 """Build libhr.so in-tree with hipcc for gfx950.
 
-Usage: python -m hadamard_rotation_int4_amd.build   (or call build()).
+Usage: python hadamard_rotation_int4_amd/build.py   (or call build()).  Run it as
+a script (or load it by path): importing the package first would try to load
+the very library this builds.
 Each .hip file under csrc/ is compiled to an object in parallel, then linked
 into hadamard_rotation_int4_amd/libhr.so.
 """

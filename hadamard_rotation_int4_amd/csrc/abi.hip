@@ -205,6 +205,101 @@ int32_t hr_butterfly_apply(const float* x, float* y, int64_t rows, int32_t n, co
   return from_hip(hr::launch_butterfly(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+// Checks a HARP schedule given on the host and fills the per-stage offsets.
+static int32_t harp_schedule(const char* fn, const int32_t* radices, int32_t nstages, int32_t* d_out,
+                             hr::HarpSchedule* sc) {
+  if (!radices) return fail(HR_EINVAL, "%s: radices is NULL", fn);
+  if (nstages < 1 || nstages > hr::kHarpMaxStages)
+    return fail(HR_EUNSUPPORTED, "%s: nstages=%d outside [1, %d]", fn, nstages, hr::kHarpMaxStages);
+  int64_t d = 1;
+  for (int t = 0; t < nstages; ++t) {
+    if (radices[t] < 2 || radices[t] > hr::kHarpMaxRadix)
+      return fail(HR_EUNSUPPORTED, "%s: radix %d of stage %d outside [2, %d]", fn, radices[t], t,
+                  hr::kHarpMaxRadix);
+    d *= radices[t];
+    if (d > 16384) return fail(HR_EUNSUPPORTED, "%s: the radices multiply past 16384", fn);
+  }
+  if (d % 4) return fail(HR_EUNSUPPORTED, "%s: d=%lld is not a multiple of 4", fn, (long long)d);
+  *sc = hr::HarpSchedule{};
+  sc->nstages = nstages;
+  int64_t stride = 1, nblk = 0, th = 0, fb = 0, bo = 0;
+  for (int t = 0; t < nstages; ++t) {
+    const int b = radices[t];
+    sc->radix[t] = b;
+    sc->stride[t] = (int)stride;
+    sc->block_begin[t] = nblk;
+    sc->theta_off[t] = th;
+    sc->fallback_off[t] = fb;
+    sc->blocks_off[t] = bo;
+    stride *= b;
+    nblk += d / b;
+    th += (d / b) * (b == 2 ? 1 : b * (b - 1) / 2);
+    if (!pow2(b)) fb += (int64_t)b * b;
+    bo += d * b;
+  }
+  sc->block_begin[nstages] = nblk;
+  *d_out = (int32_t)d;
+  return HR_OK;
+}
+
+int32_t hr_harp_blocks(const int32_t* radices, int32_t nstages, const float* theta,
+                       const float* fallbacks, float* blocks, void* stream) {
+  const char* fn = "hr_harp_blocks";
+  hr::HarpSchedule sc;
+  int32_t d = 0;
+  const int32_t st = harp_schedule(fn, radices, nstages, &d, &sc);
+  if (st) return st;
+  bool need_fb = false;
+  for (int t = 0; t < nstages; ++t) need_fb |= !pow2(radices[t]);
+  if (!theta || !blocks) return fail(HR_EINVAL, "%s: theta and blocks are required", fn);
+  if (need_fb && !fallbacks)
+    return fail(HR_EINVAL, "%s: a radix is not a power of two but fallbacks is NULL", fn);
+  if (!aligned16(theta) || !aligned16(blocks) || (fallbacks && !aligned16(fallbacks)))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  return from_hip(hr::launch_harp_blocks(sc, theta, fallbacks, blocks, static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int32_t hr_harp_apply(const float* x, float* y, int64_t rows, const int32_t* radices, int32_t nstages,
+                      const float* blocks, int32_t inverse, int32_t group, uint8_t* codes,
+                      void* scales, int32_t scale_dtype, void* stream) {
+  const char* fn = "hr_harp_apply";
+  hr::HarpSchedule sc;
+  int32_t d = 0;
+  const int32_t st = harp_schedule(fn, radices, nstages, &d, &sc);
+  if (st) return st;
+  if (rows < 0) return fail(HR_EINVAL, "%s: rows < 0", fn);
+  if (!blocks) return fail(HR_EINVAL, "%s: blocks is required", fn);
+  if (!x && rows > 0) return fail(HR_EINVAL, "%s: x is NULL", fn);
+  if (!y && !codes && rows > 0) return fail(HR_EINVAL, "%s: y and codes are both NULL", fn);
+  if (!codes && scales) return fail(HR_EINVAL, "%s: scales given without codes", fn);
+  if (codes && !scales) return fail(HR_EINVAL, "%s: codes given without scales", fn);
+  if (!aligned16(x) || (y && !aligned16(y)) || !aligned16(blocks) || (codes && !aligned16(codes)) ||
+      (scales && !aligned16(scales)))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (inverse != 0 && inverse != 1) return fail(HR_EINVAL, "%s: inverse must be 0 or 1", fn);
+  if (codes) {
+    if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+      return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+    if (!valid_group(group) || d % group)
+      return fail(HR_EUNSUPPORTED, "%s: group=%d invalid for d=%d", fn, group, d);
+  }
+  if (rows == 0) return ok();
+  hr::HarpArgs a{};
+  a.x = x;
+  a.y = y;
+  a.rows = rows;
+  a.d = d;
+  a.sc = sc;
+  a.blocks = blocks;
+  a.inverse = inverse;
+  a.group = group;
+  a.codes = codes;
+  a.scales = scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  return from_hip(hr::launch_harp_apply(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 int32_t hr_dequant_int4(const uint8_t* codes, const void* scales, int32_t scale_dtype, int64_t rows,
                         int32_t n, int32_t group, float* out, void* stream) {
   const char* fn = "hr_dequant_int4";

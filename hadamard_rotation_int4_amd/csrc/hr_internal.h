@@ -51,6 +51,39 @@ struct GemmArgs {
   int32_t* group_acc;
 };
 
+constexpr int kHarpMaxStages = 16;
+constexpr int kHarpMaxRadix = 8;
+
+// A mixed-radix schedule with its per-stage offsets (filled on the host).
+struct HarpSchedule {
+  int nstages;
+  int radix[kHarpMaxStages];
+  int stride[kHarpMaxStages];               // b_0 ... b_{t-1}
+  int64_t block_begin[kHarpMaxStages + 1];  // global index of the first block of each stage
+  int64_t theta_off[kHarpMaxStages];        // floats into theta
+  int64_t fallback_off[kHarpMaxStages];     // floats into fallbacks (radices not a power of two)
+  int64_t blocks_off[kHarpMaxStages];       // floats into the block table
+};
+
+struct HarpArgs {
+  const float* x;
+  float* y;              // fp32 output or null
+  int64_t rows;
+  int d;
+  HarpSchedule sc;
+  const float* blocks;
+  int inverse;
+  int group;
+  uint8_t* codes;        // packed int4 output or null
+  void* scales;
+  int scale_f16;
+  int rows_per_group;    // set by the launcher
+};
+
+hipError_t launch_harp_blocks(const HarpSchedule& sc, const float* theta, const float* fallbacks,
+                              float* blocks, hipStream_t s);
+hipError_t launch_harp_apply(HarpArgs a, hipStream_t s);
+
 hipError_t launch_rht(const RhtArgs& a, hipStream_t s);
 bool launch_rht2048(const RhtArgs& a, hipStream_t s);  // false: not handled
 bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s);  // false: not handled

@@ -202,6 +202,63 @@ int32_t hr_butterfly_apply(const float* x, float* y, int64_t rows, int32_t n,
                            void* stream);
 
 /*
+ * hr_harp_blocks -- the dense blocks B_{t,c} = Q_{t,c}(theta) G_{b_t} of a HARP
+ * processor with a general mixed-radix schedule (run once per set of
+ * parameters).
+ *
+ * Defines: HARP technical summary, section 2.1 (a mixed-radix schedule
+ * b = (b_0 .. b_{m-1}) with prod b_t = d, e.g. 5120 = (8, 8, 8, 5, 2); radices
+ * that are not powers of two use a fixed orthogonal fallback from the QR
+ * factorisation of a Gaussian matrix) and section 2.2 (B = Q(theta) G_b, Q a
+ * Givens rotation for b = 2 and the Cayley map for b > 2, G_b the normalised
+ * Sylvester-Hadamard matrix for powers of two; theta = 0 gives B = G_b).
+ *
+ * Stage t has d / b_t blocks.  Its parameters are [d/b_t][P_t] floats,
+ * P_t = 1 for b_t = 2 (the angle th: Q = [[cos th, -sin th], [sin th, cos th]])
+ * and b_t (b_t - 1) / 2 otherwise (the upper triangle A[i][j], i < j, row-major,
+ * of a skew-symmetric A; Q = (I - A)^(-1) (I + A)).  Q and the product are
+ * formed in double precision and stored as fp32.
+ *
+ *   radices    HOST array [nstages] int32, each in [2, 8]; their product d is a
+ *              multiple of 4 and at most 16384; 1 <= nstages <= 16.
+ *   theta      [sum_t (d / b_t) P_t] fp32, stages concatenated in order.
+ *   fallbacks  [b][b] fp32 orthogonal matrices (row-major), one per stage whose
+ *              radix is not a power of two, concatenated in stage order; may be
+ *              NULL when every radix is a power of two.  Used as given.
+ *   blocks     output [sum_t d * b_t] fp32, stages concatenated in order; stage t
+ *              is coefficient-major, [b_t][b_t][d/b_t]: entry (r, q) of block c
+ *              at (r * b_t + q) * (d / b_t) + c.
+ */
+int32_t hr_harp_blocks(const int32_t* radices, int32_t nstages, const float* theta,
+                       const float* fallbacks, float* blocks, void* stream);
+
+/*
+ * hr_harp_apply -- apply a HARP processor (or its transpose) to every row,
+ * optionally fused with int4 quantization of the result.
+ *
+ * Defines: as hr_harp_blocks, plus section 2.4 of the same summary (stages
+ * applied in O(d log d) work without materialised permutations).
+ *
+ * Write a coordinate as i = sum_t i_t S_t, S_t = b_0 ... b_{t-1}.  Forward
+ * (inverse == 0): stages t = 0 .. m-1; block c = lo + S_t hi (lo < S_t) of
+ * stage t maps the coordinates i_r = lo + S_t (r + b_t hi), r < b_t, by
+ * y_{i_r} = sum_q B_{t,c}[r][q] x_{i_q}.  Inverse (inverse == 1): the
+ * transpose, stages t = m-1 .. 0 with B^T.  With all radices 2 this is
+ * hr_butterfly_apply with precondition = 1 and no permutation.
+ *
+ *   x       [rows][d] fp32.
+ *   y       [rows][d] fp32 output, or NULL to skip it; y == x is allowed.
+ *   radices, nstages  the schedule, as for hr_harp_blocks (HOST array).
+ *   blocks  the table from hr_harp_blocks for the same schedule.
+ *   codes, scales, group, scale_dtype: as hr_rotate_quant_int4, quantizing the
+ *           processor's output; codes == NULL skips quantization (scales must
+ *           then be NULL).  At least one of y and codes must be non-NULL.
+ */
+int32_t hr_harp_apply(const float* x, float* y, int64_t rows, const int32_t* radices,
+                      int32_t nstages, const float* blocks, int32_t inverse, int32_t group,
+                      uint8_t* codes, void* scales, int32_t scale_dtype, void* stream);
+
+/*
  * hr_dequant_int4 -- x_hat = q * s per element (one fp32 product, so the result
  * is bit-exact).
  *

@@ -146,3 +146,41 @@ def test_gemm_validation(fn):
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 256, 128, P, P + 4, None) == hr.HR_EINVAL
     assert f(P, P, P, P, hr.HR_F16, 0, 64, 256, 128, P, None, None) == hr.HR_OK
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 131072, 128, P, None, None) == hr.HR_EUNSUPPORTED
+
+
+def _rad(*b):
+    return (ctypes.c_int32 * len(b))(*b), len(b)
+
+
+def test_harp_validation():
+    ap, bl = hr.lib.hr_harp_apply, hr.lib.hr_harp_blocks
+    r, m = _rad(8, 8, 8, 5, 2)
+    # x, y, rows, radices, nstages, blocks, inverse, group, codes, scales, sdt, stream
+    assert ap(None, P, 4, r, m, P, 0, 0, None, None, 0, None) == hr.HR_EINVAL
+    assert ap(P, None, 4, r, m, P, 0, 0, None, None, 0, None) == hr.HR_EINVAL
+    assert ap(P, P, -1, r, m, P, 0, 0, None, None, 0, None) == hr.HR_EINVAL
+    assert ap(P, P, 4, r, m, None, 0, 0, None, None, 0, None) == hr.HR_EINVAL
+    assert ap(P, P, 4, None, m, P, 0, 0, None, None, 0, None) == hr.HR_EINVAL
+    assert ap(P, P, 4, r, m, P, 2, 0, None, None, 0, None) == hr.HR_EINVAL
+    assert ap(P + 4, P, 4, r, m, P, 0, 0, None, None, 0, None) == hr.HR_EINVAL
+    assert ap(P, P, 4, r, m, P, 0, 96, P, P, hr.HR_F16, None) == hr.HR_EUNSUPPORTED
+    assert ap(P, P, 4, r, m, P, 0, 128, P, None, hr.HR_F16, None) == hr.HR_EINVAL
+    assert ap(P, P, 4, r, m, P, 0, 128, P, P, hr.HR_BF16, None) == hr.HR_EINVAL
+    assert ap(P, P, 0, r, m, P, 0, 0, None, None, 0, None) == hr.HR_OK
+    r9, m9 = _rad(9, 4)
+    assert ap(P, P, 4, r9, m9, P, 0, 0, None, None, 0, None) == hr.HR_EUNSUPPORTED   # radix > 8
+    r1, m1 = _rad(1, 8)
+    assert ap(P, P, 4, r1, m1, P, 0, 0, None, None, 0, None) == hr.HR_EUNSUPPORTED
+    rb, mb = _rad(8, 8, 8, 8, 8)
+    assert ap(P, P, 4, rb, mb, P, 0, 0, None, None, 0, None) == hr.HR_EUNSUPPORTED   # d > 16384
+    ro, mo = _rad(3, 5)
+    assert ap(P, P, 4, ro, mo, P, 0, 0, None, None, 0, None) == hr.HR_EUNSUPPORTED   # d % 4
+    assert ap(P, P, 4, r, 0, P, 0, 0, None, None, 0, None) == hr.HR_EUNSUPPORTED
+    assert ap(P, P, 4, r, 17, P, 0, 0, None, None, 0, None) == hr.HR_EUNSUPPORTED
+    # radices, nstages, theta, fallbacks, blocks, stream
+    assert bl(r, m, P, None, P, None) == hr.HR_EINVAL          # radix 5 needs a fallback
+    assert bl(r, m, None, P, P, None) == hr.HR_EINVAL
+    assert bl(r, m, P, P, None, None) == hr.HR_EINVAL
+    assert bl(r, m, P + 8, P, P, None) == hr.HR_EINVAL
+    assert bl(r9, m9, P, P, P, None) == hr.HR_EUNSUPPORTED
+    assert b"hr_harp_blocks" in hr.lib.hr_last_error()
