@@ -6,8 +6,13 @@
 // 2.1 (stride stages), 2.2 (block kernel Q(theta) G_2) and 2.4 (O(d log d)
 // application without materialised permutations).
 //
-// One workgroup of 512 threads per row, persistent over rows.  Each thread
-// owns 8 elements of the row per pass; the 12 stages run as 4 passes of 3
+// One workgroup of 512 threads per row, persistent over rows.  With an fp32
+// output, input rows stream through a ring of kBfRing LDS stages filled by
+// global_load_lds (kBfRing rows in flight per CU without holding registers):
+// wave w loads bytes 2048 w .. 2048 w + 2047 of a row, which are exactly the
+// 8-element slices of its own 64 threads, so a wave waits only for its own
+// loads.  With codes only, the next row is prefetched into registers.  Each
+// thread owns 8 elements of the row per pass; the 12 stages run as 4 passes of 3
 // register stages.  In pass k the thread's 8 registers are the elements whose
 // index bits 3k..3k+2 take all 8 values, the other 9 bits being the thread
 // index; between passes the row goes through LDS.  Because a thread owns the
@@ -23,6 +28,20 @@ namespace hr {
 constexpr int kBfN = 4096;
 constexpr int kBfThreads4096 = 512;
 constexpr int kBfLds = kBfN + 8 * (kBfN / 64);
+constexpr int kBfRing = 3;
+
+// Workgroup barrier for the LDS transposes: this wave's LDS accesses are
+// complete (lgkmcnt 0) before it arrives.  Unlike __syncthreads it does not
+// also wait for the ring's loads still in flight (vmcnt), which would drain
+// the prefetch at every transpose; the memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void bf_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void bf_lds_load16(const void* gp, void* lp) {
+  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+}
 
 __device__ __forceinline__ int bf_pad(int i) { return i + 8 * (i >> 6); }
 
@@ -70,7 +89,12 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
     uint8_t* __restrict__ codes, void* __restrict__ scales) {
   constexpr int N = kBfN, HALF = N / 2;
   __shared__ __attribute__((aligned(16))) float lds[2][kBfLds];
+  // the ring only where the row's fp32 output makes the kernel memory-bound;
+  // with codes only, its extra LDS traffic costs more than it hides
+  constexpr bool RING = OUT_Y;
+  __shared__ __attribute__((aligned(16))) float ring[RING ? kBfRing : 1][RING ? N : 4];
   const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
 
   // per-thread coefficients of its 4 pairs in each of the 12 stages
   float2 cf[12][4];
@@ -88,20 +112,71 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
 #pragma unroll
   for (int r = 0; r < 8; ++r) pm[r] = perm ? perm[8 * t + r] : 8 * t + r;
 
-  // the next row's 8 elements are in flight while the current row is processed
-  f32x4 n0, n1;
-  if ((int64_t)blockIdx.x < rows) {
-    const f32x4* xr = reinterpret_cast<const f32x4*>(x + (int64_t)blockIdx.x * N) + 2 * t;
-    n0 = __builtin_nontemporal_load(xr);
-    n1 = __builtin_nontemporal_load(xr + 1);
+  // row r goes to ring stage: wave wv's two loads put bytes 2048 wv + 16 lane
+  // (+ 1024) of the row at the same offsets of the stage
+  auto issue = [&](int64_t r, int st) {
+    const char* src = reinterpret_cast<const char*>(x + r * N) + 2048 * wv + 16 * lane;
+    char* dst = reinterpret_cast<char*>(&ring[st][0]) + 2048 * wv;
+    bf_lds_load16(src, dst);
+    bf_lds_load16(src + 1024, dst + 1024);
+  };
+  const int64_t step = gridDim.x;
+  if (RING) {
+#pragma unroll
+    for (int i = 0; i < kBfRing; ++i)
+      if ((int64_t)blockIdx.x + i * step < rows) issue((int64_t)blockIdx.x + i * step, i);
   }
+  // thread t's elements 8t .. 8t+7: bytes 32 t of the stage
+  const uint32_t rd_off = 32u * (uint32_t)t;
 
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    float v[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
-    if (row + gridDim.x < rows) {
-      const f32x4* xr = reinterpret_cast<const f32x4*>(x + (row + gridDim.x) * N) + 2 * t;
-      n0 = __builtin_nontemporal_load(xr);
-      n1 = __builtin_nontemporal_load(xr + 1);
+  int st = 0, iter = 0;
+  f32x4 p0, p1;       // register prefetch of the next row (without the ring)
+  if (!RING && (int64_t)blockIdx.x < rows) {
+    const f32x4* xr = reinterpret_cast<const f32x4*>(x + (int64_t)blockIdx.x * N) + 2 * t;
+    p0 = __builtin_nontemporal_load(xr);
+    p1 = __builtin_nontemporal_load(xr + 1);
+  }
+  for (int64_t row = blockIdx.x; row < rows;
+       row += step, st = st + 1 == kBfRing ? 0 : st + 1, ++iter) {
+    float v[8];
+    if (!RING) {
+      v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+      v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+      if (row + step < rows) {
+        const f32x4* xr = reinterpret_cast<const f32x4*>(x + (row + step) * N) + 2 * t;
+        p0 = __builtin_nontemporal_load(xr);
+        p1 = __builtin_nontemporal_load(xr + 1);
+      }
+    } else {
+      // wait for this row's two loads.  Vector memory operations complete in
+      // issue order; the ones issued after them are the younger rows' loads (two
+      // each) and the stores of the rows processed since: SU per row, two fp32
+      // stores and the code and scale stores.  Every wave issues each of them
+      // (a wave's 64 threads always include scale-storing ones, since G / 8 <= 32),
+      // so the count is exact.  Near the end of the rows everything is drained.
+      f32x4 n0, n1;
+      const uint32_t addr = (uint32_t)(uintptr_t)&ring[st][0] + rd_off;
+      constexpr int SU = (OUT_Y ? 2 : 0) + (G > 0 ? 2 : 0);
+#define HR_BFR(N)                                                                            \
+      asm volatile("s_waitcnt vmcnt(" #N ")\n\tds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\t" \
+                   "s_waitcnt lgkmcnt(0)"                                                     \
+                   : "=v"(n0), "=v"(n1)                                                       \
+                   : "v"(addr)                                                                \
+                   : "memory")
+      static_assert(kBfRing == 3, "the wait counts below assume three ring stages");
+      if (row + (kBfRing - 1) * step < rows) {
+        const int done = iter < kBfRing ? iter : kBfRing;   // rows processed whose stores are younger
+        static_assert(SU == 2 || SU == 4, "fp32 out, codes, or both");
+        if (done == 0) HR_BFR(4);
+        else if (SU == 2) { if (done == 1) HR_BFR(6); else if (done == 2) HR_BFR(8); else HR_BFR(10); }
+        else { if (done == 1) HR_BFR(8); else if (done == 2) HR_BFR(12); else HR_BFR(16); }
+      } else {
+        HR_BFR(0);
+      }
+#undef HR_BFR
+      v[0] = n0.x; v[1] = n0.y; v[2] = n0.z; v[3] = n0.w;
+      v[4] = n1.x; v[5] = n1.y; v[6] = n1.z; v[7] = n1.w;
+      if (row + kBfRing * step < rows) issue(row + kBfRing * step, st);
     }
     if (!INVERSE) {
       // pass 0: stages 0, 1, 2 on elements 8t .. 8t+7
@@ -112,7 +187,7 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
       for (int k = 1; k < 4; ++k) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, k - 1, r))] = v[r];
-        __syncthreads();
+        bf_barrier();
 #pragma unroll
         for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, k, r))];
 #pragma unroll
@@ -122,14 +197,29 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
       // gather: out[8t + r] = z[perm[8t + r]]
 #pragma unroll
       for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, 3, r))] = v[r];
-      __syncthreads();
+      bf_barrier();
+      if (perm) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(pm[r])];
+        for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(pm[r])];
+      } else {
+        // identity: elements 8t .. 8t+7 are 8 consecutive padded slots, read
+        // as two 16-byte loads (eight scalar loads at a stride of 8 conflict)
+        const f32x4* src = reinterpret_cast<const f32x4*>(&lds[buf][bf_pad(8 * t)]);
+        const f32x4 u0 = src[0], u1 = src[1];
+        v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+        v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+      }
     } else {
       // scatter z[perm[i]] = x[i], then the transposed stages in reverse order
+      if (perm) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) lds[0][bf_pad(pm[r])] = v[r];
-      __syncthreads();
+        for (int r = 0; r < 8; ++r) lds[0][bf_pad(pm[r])] = v[r];
+      } else {
+        f32x4* dst = reinterpret_cast<f32x4*>(&lds[0][bf_pad(8 * t)]);
+        dst[0] = (f32x4){v[0], v[1], v[2], v[3]};
+        dst[1] = (f32x4){v[4], v[5], v[6], v[7]};
+      }
+      bf_barrier();
       int buf = 0;
 #pragma unroll
       for (int k = 3; k >= 1; --k) {
@@ -140,7 +230,7 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
         buf ^= 1;
 #pragma unroll
         for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, k, r))] = v[r];
-        __syncthreads();
+        bf_barrier();
       }
 #pragma unroll
       for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, 0, r))];

@@ -248,6 +248,28 @@ def test_butterfly_quant(group, scale_mode):
     check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, scale_mode)
 
 
+@pytest.mark.parametrize("precondition", [False, True])
+def test_butterfly_4096_many_rows_identity_perm(precondition):
+    """About five rows per workgroup (the input ring wraps and reaches its
+    steady-state waits), no permutation (the vector gather and scatter), and
+    both outputs at once; sampled rows against the oracle."""
+    hr = _hr()
+    rows, n = 1300, 4096
+    bi = hr_inputs.butterfly_inputs(rows=rows, n=n, seed=460 + int(precondition))
+    co = hr.butterfly_coeffs(torch.from_numpy(bi.angles).to(DEV), precondition)
+    xd = torch.from_numpy(bi.x).to(DEV)
+    y, codes, scales = hr.butterfly_apply(xd, co, precondition, None, group=64)
+    yi = hr.butterfly_apply(xd, co, precondition, None, inverse=True)
+    sample = np.unique(np.concatenate([np.random.default_rng(5).choice(rows, 40, replace=False),
+                                       [0, 255, 256, 767, 768, rows - 1]]))
+    xs = bi.x[sample]
+    y64 = oracle.butterfly.butterfly(xs, bi.angles, None, precondition)
+    check_rotated(y.cpu().numpy()[sample], y64)
+    check_quant(codes.cpu().numpy()[sample], scales.cpu().numpy()[sample], y64, 64, "f16")
+    inv64 = oracle.butterfly.butterfly(xs, bi.angles, None, precondition, inverse=True)
+    check_rotated(yi.cpu().numpy()[sample], inv64)
+
+
 # ---------------------------------------------------------------- dequant
 
 @pytest.mark.parametrize("group,scale_mode", [(32, "f16"), (128, "f16"), (256, "f32")])
