@@ -44,6 +44,8 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
   // LDS of this wave: two row stages (256 slots of 16 bytes) and one row of codes
   __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][2][256];
   __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][BITS == 8 ? 128 : 64];
+  // fp32 output: this wave's 8 KB output row, staged so it leaves as 1 KB stores
+  __shared__ __attribute__((aligned(16))) f32x4 out_lds[OUT_F32 ? 4 : 1][OUT_F32 ? 512 : 1];
   // element offset of this lane's piece within a row, per load j: + 32 j
   const int lane_src = 128 * (lane & 15) + 8 * (lane >> 4);
   auto issue = [&](int64_t row, int st) {
@@ -77,14 +79,25 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
     mfma2048_transform(M, b, acc);
     // lane now holds tau * Y[a4][c], c = v + 4 T0 + 8 g + 32 T1 + 64 T2
     if (OUT_F32) {
+      // 16-byte slot 32 a + s of the row (s = 8 m + 2 g + h) sits at 32 a +
+      // (s ^ a): the lanes of a write phase, which differ in a, then hit
+      // different bank groups, and a lane's read phase stays inside one a
       const float ym = norm * tau;
+      f32x4* ol = &out_lds[wib][0];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        f32x4* dst = reinterpret_cast<f32x4*>(yout + row * N + 128 * a4 + 32 * m + 8 * g);
         const f32x4 lo = acc[2 * m], hi = acc[2 * m + 1];
-        dst[0] = (f32x4){lo[0] * ym, lo[1] * ym, lo[2] * ym, lo[3] * ym};
-        dst[1] = (f32x4){hi[0] * ym, hi[1] * ym, hi[2] * ym, hi[3] * ym};
+        ol[32 * a4 + ((8 * m + 2 * g) ^ a4)] = (f32x4){lo[0] * ym, lo[1] * ym, lo[2] * ym, lo[3] * ym};
+        ol[32 * a4 + ((8 * m + 2 * g + 1) ^ a4)] = (f32x4){hi[0] * ym, hi[1] * ym, hi[2] * ym, hi[3] * ym};
       }
+      __builtin_amdgcn_wave_barrier();
+      f32x4* dst = reinterpret_cast<f32x4*>(yout + row * N);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int sl = 64 * i + lane, a = sl >> 5;
+        __builtin_nontemporal_store(ol[32 * a + ((sl & 31) ^ a)], dst + sl);
+      }
+      __builtin_amdgcn_wave_barrier();
       return;
     }
     // group absmax: run m (outputs 32 m + 8 g + 0..7) is tiles 2m, 2m+1
