@@ -299,6 +299,27 @@ def main(argv=None):
                 "GB/s": byts / msg / 1e6, "ops": ops, "bytes": byts,
                 "timing": "eager launches" if M > 16 else "HIP graph of 20 launches, replayed"}
 
+        # one decode step with online rotation: the 16 activation rows (bf16, K =
+        # 4096) are rotated and quantized, then multiplied by the int4 weights;
+        # both launches in one graph, against the GEMM alone above
+        gi = hr_inputs.gemm_inputs(M=16)
+        wd, swd = (torch.from_numpy(gi.w_codes).to(dev), torch.from_numpy(gi.w_scales).to(dev))
+        ri = hr_inputs.rht_inputs(rows=16, n=4096, seed=7)
+        xa, da = ri.x.to(dev), torch.from_numpy(ri.signs).to(dev)
+        ac = torch.empty((16, 2048), dtype=torch.uint8, device=dev)
+        asc = torch.empty((16, 32), dtype=torch.float16, device=dev)
+        cg = torch.empty((16, 4096), dtype=torch.float32, device=dev)
+
+        def decode_step(i):
+            hr.rotate_quant_int4(xa, 128, da, codes=ac, scales=asc)
+            hr.w4a4_gemm(ac, asc, wd, swd, 128, out=cg)
+
+        msd = _timed_graph(decode_step, args.steps, args.warmup)
+        msg16 = kernels["w4a4_gemm_16x4096x4096_g128"]["ms"]
+        kernels["decode_step_rotate_quant_w4a4_16x4096x4096_g128"] = {
+            "ms": msd, "gemm_alone_ms": msg16, "rotation_overhead": msd / msg16 - 1.0,
+            "timing": "HIP graph of 20 steps (2 launches each), replayed"}
+
         # W4A8 GEMM: int8 activations, the same int4 weights
         for M in (4096, 16):
             gi = hr_inputs.gemm_w4a8_inputs(M=M)

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void rht2048_kernel(const void* __restrict__ x
   }
 }
 
-template <bool IN_BF16, int G, bool SCALE_F16, bool OUT_F32>
+template <bool IN_BF16, int G, bool SCALE_F16, bool OUT_F32, bool SYLV = false>
 __global__ __launch_bounds__(1024) void mixed2048_kernel(const void* __restrict__ xin,
                                                           const int8_t* __restrict__ signs,
                                                           const float* __restrict__ block, int m,
@@ -76,9 +76,12 @@ __global__ __launch_bounds__(1024) void mixed2048_kernel(const void* __restrict_
   const int64_t n = (int64_t)m * P;
   Lane2048 L;
   lane2048_init(L, signs ? signs + (int64_t)w * P : nullptr);
-  float o[16];                                  // row w of the orthogonal block
+  // row w of the block: the given orthogonal O, or (SYLV) the +-1 Sylvester
+  // matrix H_m, so that H_m kron H_2048 = H_{m 2048} exactly
+  float o[16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) o[c] = c < m ? block[w * m + c] : 0.0f;
+  for (int c = 0; c < 16; ++c)
+    o[c] = c < m ? (SYLV ? ((__builtin_popcount(w & c) & 1) ? -1.0f : 1.0f) : block[w * m + c]) : 0.0f;
 
   u32x4 nxt[4];
   if (IN_BF16 && (int64_t)blockIdx.x < rows)
@@ -140,6 +143,17 @@ __global__ __launch_bounds__(1024) void mixed2048_kernel(const void* __restrict_
 
 template <bool IN_BF16, int G, bool SCALE_F16, bool OUT_F32>
 static void launch_one(const RhtArgs& a, float norm, hipStream_t s) {
+  if (a.p > 2048) {
+    // p = m' * 2048 with m = 1: the mixed-radix kernel with the Sylvester block
+    const int mm = a.p / 2048;
+    const size_t lds = (size_t)mm * 2048 * sizeof(float);
+    const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+    const int64_t blocks = a.rows < 256 * per_cu ? a.rows : 256 * per_cu;
+    hipLaunchKernelGGL((mixed2048_kernel<IN_BF16, G, SCALE_F16, OUT_F32, true>), dim3((unsigned)blocks),
+                       dim3(64 * mm), lds, s, a.x, a.signs, (const float*)nullptr, mm, a.rows, a.y,
+                       a.codes, a.scales, norm);
+    return;
+  }
   if (a.m == 1) {
     int64_t blocks = (a.rows + 3) / 4;   // one wave per row, 4 waves per block
     const int64_t cap = 256 * HR_RHT2048_BLOCKS_PER_CU;
@@ -179,11 +193,17 @@ static bool dispatch_in(const RhtArgs& a, float norm, hipStream_t s) {
 #undef HR_Q
 }
 
-// Handles p == 2048 (n = m * 2048, 1 <= m <= 16), fp32 output or fused
-// quantization.  Returns false when the case belongs to the general kernel.
+// Handles p == 2048 (n = m * 2048, 1 <= m <= 16), and the plain transform of
+// p = 4096, 8192, 16384 (m = 1) as H_{p/2048} kron H_2048; fp32 output or
+// fused int4 quantization.  Returns false when the case belongs to the
+// general kernel.
 bool launch_rht2048(const RhtArgs& a, hipStream_t s) {
-  if (a.p != 2048 || a.m < 1 || a.m > 16) return false;
   if (a.codes && a.bits == 8) return false;     // int8 codes: generic kernel
+  if (a.m == 1 && (a.p == 4096 || a.p == 8192 || a.p == 16384)) {
+    const float norm = (float)(1.0 / sqrt((double)a.p));
+    return a.x_bf16 ? dispatch_in<true>(a, norm, s) : dispatch_in<false>(a, norm, s);
+  }
+  if (a.p != 2048 || a.m < 1 || a.m > 16) return false;
   if (a.m > 1 && (size_t)a.m * 2048 * sizeof(float) > 160 * 1024) return false;
   const float norm = (float)(1.0 / sqrt(2048.0));
   return a.x_bf16 ? dispatch_in<true>(a, norm, s) : dispatch_in<false>(a, norm, s);
