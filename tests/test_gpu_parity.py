@@ -352,6 +352,20 @@ def test_gemm_decode_shapes(M, N, K, group, scale_mode):
     assert torch.equal(c2, c)
 
 
+@pytest.mark.parametrize("M,N,group", [(3, 64, 256), (17, 128, 128), (40, 192, 64)])
+def test_gemm_max_k(M, N, group):
+    """K = 65536, the largest the library accepts: decode, prefill and simple kernels."""
+    hr = _hr()
+    K = 65536
+    gi = hr_inputs.gemm_inputs(M=M, N=N, K=K, group=group, seed=1200 + M)
+    t = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    c, acc = hr.w4a4_gemm(t(gi.a_codes), t(gi.a_scales), t(gi.w_codes), t(gi.w_scales), group,
+                          group_acc=True)
+    c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(gi.a_codes, gi.a_scales, gi.w_codes, gi.w_scales,
+                                                  group, return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
+
+
 def test_gemm_fp32_scales_and_minus_eight():
     hr = _hr()
     M, N, K, group = 33, 128, 512, 128
