@@ -148,6 +148,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="time only the headline kernel")
+    ap.add_argument("--profile-gemm", action="store_true",
+                    help="run only the 4096^3 W4A4 and W4A8 GEMMs, --steps times each (for counters)")
     ap.add_argument("--profile-run", action="store_true",
                     help="run the headline kernel and a plain copy (for rocprofv3 --pmc), print nothing")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -178,6 +180,19 @@ def main(argv=None):
 
     def step(i):
         hr.rotate_quant_int4(xs[i], GROUP, d, codes=codes[i], scales=scales[i])
+
+    if args.profile_gemm:
+        gi = hr_inputs.gemm_inputs(M=4096)
+        g8 = hr_inputs.gemm_w4a8_inputs(M=4096)
+        t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+        wd, swd = t(gi.w_codes), t(gi.w_scales)
+        cg = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+        for call, a_codes, a_scales in ((hr.w4a4_gemm, t(gi.a_codes), t(gi.a_scales)),
+                                        (hr.w4a8_gemm, t(g8.a_codes), t(g8.a_scales))):
+            for _ in range(args.steps):
+                call(a_codes, a_scales, wd, swd, 128, out=cg)
+        torch.cuda.synchronize()
+        return 0
 
     if args.profile_run:
         for i in range(args.steps):
@@ -356,6 +371,15 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": load_traffic()},
     }
+    if not args.only_main:
+        # a plain elementwise pass over COPY_BYTES (read and write) as the
+        # practical HBM ceiling of the box the line was measured on
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        msc = _timed(lambda i: torch.neg(src, out=dst), 20, 5)
+        out["practical_ceiling"] = {"kernel": "torch.neg over 512 MiB bf16 (read + write)",
+                                    "GB/s": round(2 * COPY_BYTES / msc / 1e6, 1)}
+        del src, dst
     g4096 = kernels.get("w4a4_gemm_4096x4096x4096_g128")
     if g4096:
         out["w4a4_gemm_tops"] = round(g4096["TOPS"], 1)
@@ -380,6 +404,52 @@ def _counter_per_dispatch(rows, kernel_substr, counter):
     vals = [float(r["Counter_Value"]) for r in rows
             if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+GEMM_COUNTER_PASSES = (
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES",
+    "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY "
+    "SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_INSTS_VMEM_RD",
+)
+
+
+def _summarize_gemm_counters(d):
+    """Per-dispatch counter averages of the two 4096^3 tile kernels, from the
+    passes under d/gemm_p1, d/gemm_p2 (one rocprofv3 --pmc run each)."""
+    rows = []
+    for i in range(1, len(GEMM_COUNTER_PASSES) + 1):
+        rows += _read_csv(os.path.join(d, f"gemm_p{i}", "**", "*counter_collection.csv"))
+    if not rows:
+        return
+    lines = ["# rocprofv3 --pmc counters, per dispatch, of the 4096^3 G=128 fp16-scale GEMM tile kernels",
+             "# command, one per pass: rocprofv3 --pmc <pass> -d <dir>/gemm_p<i> -o run --output-format csv "
+             "-- python bench.py --profile-gemm --steps 10"]
+    for i, pmc in enumerate(GEMM_COUNTER_PASSES, 1):
+        lines.append(f"# pass {i}: {pmc}")
+    for label, name in (("W4A4", "w4a4_gemm_tile_kernel<128, true, false, false>"),
+                        ("W4A8", "w4a4_gemm_tile_kernel<128, true, false, true>")):
+        vals = {}
+        for pmc in " ".join(GEMM_COUNTER_PASSES).split():
+            v, n = _counter_per_dispatch(rows, name, pmc)
+            if v is not None:
+                vals[pmc] = v
+        if not vals:
+            continue
+        lines.append(f"{label} ({name}):")
+        for k, v in vals.items():
+            lines.append(f"  {k} = {v:.6g}")
+        mf, va = vals.get("SQ_INSTS_MFMA"), vals.get("SQ_INSTS_VALU")
+        if mf and va:
+            lines.append(f"  VALU instructions per MFMA = {va / mf:.2f}")
+        bc, al = vals.get("SQ_LDS_BANK_CONFLICT"), vals.get("SQ_ACTIVE_INST_LDS")
+        if bc is not None and al:
+            lines.append(f"  LDS bank-conflict cycles / LDS-active cycles = {bc / al:.4f}")
+        mb, co = vals.get("SQ_VALU_MFMA_BUSY_CYCLES"), vals.get("SQ_VALU_MFMA_COEXEC_CYCLES")
+        if mb and co is not None:
+            lines.append(f"  VALU co-issued during MFMA-busy cycles = {co / mb:.4f}")
+    with open(os.path.join(PROFILES, "w4a4_w4a8_gemm_4096_g128.counters.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def summarize_profile(d):
@@ -417,6 +487,7 @@ def summarize_profile(d):
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": nk,
            "copy_kernel_match": copy_kernel, "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf,
            "copy_write_kib": cw, "copy_dispatches": nc}
+    _summarize_gemm_counters(d)
     if None not in (kf, kw, cf, cw):
         ff = COPY_BYTES / (cf * 1024.0)
         fw = COPY_BYTES / (cw * 1024.0)

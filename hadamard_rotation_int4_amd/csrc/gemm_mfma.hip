@@ -82,6 +82,18 @@ __device__ __forceinline__ constexpr int row_xor(int q) {
   return PPR == 4 ? (q == 0 ? 0 : q == 1 ? 6 : q == 2 ? 10 : 12) : (q == 0 ? 0 : 12);
 }
 
+// XOR applied to the row index of int8 A chunk c (PPA = 16-byte A pieces per
+// row and stage, one chunk each).  A store phase covers one row (8 lanes,
+// PPA = 8) or two rows (PPA = 4) times the PPA chunks, or twice that for 16
+// lanes; its 16-byte bank groups must differ modulo 8 (8 lanes) and modulo 16
+// (16 lanes).  2c + (c >> 2) = {0, 2, 4, 6, 9, 11, 13, 15} (PPA = 8) and
+// 4c + 2 (c >> 1) = {0, 4, 10, 14} (PPA = 4) do both; reads take one chunk of
+// 8 or 16 consecutive rows, which an XOR below 16 only permutes.
+template <int PPA>
+__device__ __forceinline__ constexpr int a8_xor(int c) {
+  return PPA == 8 ? 2 * c + (c >> 2) : 4 * c + 2 * (c >> 1);
+}
+
 template <int V>
 struct IntC { static constexpr int value = V; };
 
@@ -169,15 +181,13 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
   // LDS byte offsets: this thread's store slot (chunk 2 spc, row srow), and
   // the fragment read slots of K-step ks (chunk 2 ks + h, row wm + l32 or
   // wn + l32) within an operand stage.  int8 A pieces are one chunk each
-  // (chunk spc_a); their rows are XORed with spc_a * 16 / PPA, which keeps
-  // the 8- and 16-lane store phases (one or two rows, PPA chunks) and the
-  // read phases free of bank conflicts.
+  // (chunk spc_a), rows XORed with a8_xor<PPA>(chunk).
   const int st_off = (2 * spc * 128 + (srow ^ row_xor<PPR>(spc))) * 16;
-  const int st_off_a = (spc_a * 128 + (srow_a ^ (spc_a * (16 / PPA)))) * 16;
+  const int st_off_a = (spc_a * 128 + (srow_a ^ a8_xor<PPA>(spc_a))) * 16;
   int rd_a[STEPS], rd_b[STEPS];
 #pragma unroll
   for (int ks = 0; ks < STEPS; ++ks) {
-    const int xa = A8 ? (2 * ks + h) * (16 / PPA) : row_xor<PPR>(ks);
+    const int xa = A8 ? a8_xor<PPA>(2 * ks + h) : row_xor<PPR>(ks);
     rd_a[ks] = (h * 128 + wm + (l32 ^ xa)) * 16;
     rd_b[ks] = OPB + (h * 128 + wn + (l32 ^ row_xor<PPR>(ks))) * 16;
   }
