@@ -87,6 +87,7 @@ hipError_t launch_harp_apply(HarpArgs a, hipStream_t s);
 hipError_t launch_rht(const RhtArgs& a, hipStream_t s);
 bool launch_rht2048(const RhtArgs& a, hipStream_t s);  // false: not handled
 bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s);  // false: not handled
+bool launch_mixed2048_mfma(const RhtArgs& a, hipStream_t s);  // false: not handled
 hipError_t launch_butterfly_coeffs(const float* angles, int n, int log2n, int precondition,
                                    float* coeffs, hipStream_t s);
 hipError_t launch_butterfly(const ButterflyArgs& a, hipStream_t s);

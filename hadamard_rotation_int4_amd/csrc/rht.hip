@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kGenericThreads) void rht_generic_kernel(RhtArgs a,
 
 hipError_t launch_rht(const RhtArgs& a, hipStream_t s) {
   if (launch_rht2048_mfma(a, s)) return hipGetLastError();
+  if (launch_mixed2048_mfma(a, s)) return hipGetLastError();
   if (launch_rht2048(a, s)) return hipGetLastError();
   const float norm = (float)(1.0 / sqrt((double)a.p));
   const int64_t grid64 = a.rows < 4096 ? a.rows : 4096;

@@ -93,7 +93,8 @@ def test_rotate_zero_rows():
 # ------------------------------------------------------- rotate + quantize
 
 @pytest.mark.parametrize("n,group", [(2048, 128), (2048, 32), (2048, 64), (2048, 256), (64, 32),
-                                     (256, 64), (1024, 256), (4096, 128), (16384, 128)])
+                                     (256, 64), (1024, 256), (4096, 128), (16384, 128), (4096, 256),
+                                     (8192, 32)])
 @pytest.mark.parametrize("scale_mode", ["f16", "f32"])
 def test_rotate_quant(n, group, scale_mode):
     hr = _hr()
@@ -170,7 +171,8 @@ def test_mixed_radix(m, p, group):
 
 
 @pytest.mark.parametrize("m,group,with_signs,scale_mode", [(7, 128, True, "f16"), (4, 64, False, "f32"),
-                                                          (6, 256, True, "f32")])
+                                                          (6, 256, True, "f32"), (5, 32, True, "f32"),
+                                                          (8, 128, True, "f16"), (3, 64, True, "f16")])
 def test_mixed_radix_many_rows(m, group, with_signs, scale_mode):
     """More rows than resident workgroups (each workgroup loops over rows),
     with and without the sign diagonal, fp16 and fp32 scales."""
