@@ -92,7 +92,9 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
       u32x4 b[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) b[s] = nxt[s];
-      if (row + gridDim.x < rows) load_chunk(row + gridDim.x, nxt);
+      // unconditional (past the end the row reloads itself, never used): a
+      // merge of loaded and unloaded registers would wait for this load
+      load_chunk(row + gridDim.x < rows ? row + gridDim.x : row, nxt);
       Mfma2048 Mt;
       Mt.sm[0] = Mc.sm[0];
       Mt.sm[1] = Mc.sm[1];
