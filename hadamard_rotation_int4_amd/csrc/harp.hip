@@ -16,7 +16,7 @@
 // block c at (r b + q) d/b + c, so the lanes of a wave, which own consecutive
 // blocks, read each coefficient as one contiguous 256-byte run.
 // harp_apply_kernel: a persistent workgroup keeps R rows in LDS and runs
-// every stage over them; each thread takes blocks c = tid, tid + 512, ...,
+// every stage over them; each thread takes blocks c = tid, tid + 1024, ...,
 // holds the block's b^2 coefficients in registers while it maps that block of
 // all R rows, so the coefficient table (d * sum b_t floats, read from L2) is
 // fetched once per R rows.  Quantization (int4, per group) is fused at the end.
@@ -26,7 +26,9 @@
 
 namespace hr {
 
-constexpr int kHarpThreads = 512;
+// 1024 threads: the radix-8 stages of d = 5120 (640 blocks) and its radix-5
+// stage (1024 blocks) each take one round (with 512 threads the radix-8 stages took two rounds: 96 us against 89 us)
+constexpr int kHarpThreads = 1024;
 
 // LDS position of in-row element i when 64 divides d: bits 2-5 XORed with
 // bits 6-9 of i, a permutation inside every aligned block of 64 elements.
@@ -203,18 +205,22 @@ hipError_t launch_harp_blocks(const HarpSchedule& sc, const float* theta, const 
 }
 
 hipError_t launch_harp_apply(HarpArgs a, hipStream_t s) {
-  // as many rows per group as fit in 64 KB of LDS (at most 8), two
-  // workgroups per CU so that one's loads and stores overlap the other's stages
-  int R = (int)(16384 / a.d);
+  // as many rows per group as fit in 160 KB of LDS (at most 8), one
+  // workgroup per CU: every group re-reads the whole coefficient table from
+  // L2, which outweighs overlapping two workgroups' loads with each other's
+  // stages (d = 5120: 8 rows per group, 96 us, against 3 rows and two
+  // workgroups, 120 us)
+  int R = (int)(40960 / a.d);
   if (R > 8) R = 8;
   if (R < 1) R = 1;
   a.rows_per_group = R;
   const int64_t ngroups = (a.rows + R - 1) / R;
   const int64_t grid = ngroups < 512 ? ngroups : 512;
   const size_t lds = sizeof(float) * (size_t)R * a.d;
-  // more than 64 KB of dynamic LDS must be allowed explicitly
+  // more than 64 KB of dynamic LDS must be allowed explicitly (160 KB per
+  // workgroup on gfx950)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(harp_apply_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(harp_apply_kernel, dim3((unsigned)grid), dim3(kHarpThreads), lds, s, a);
   return hipGetLastError();
