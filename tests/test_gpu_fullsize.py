@@ -84,6 +84,38 @@ def test_butterfly_32768x4096():
     check_rotated(back[rd].cpu().numpy(), bi.x[rows].astype(np.float64))
 
 
+def test_butterfly_32768x4096_bench_variants():
+    """The two launches the bench times: fp32 output only, and codes only
+    (G = 64); they are other kernel instances than the combined call above."""
+    hr = _hr()
+    bi = hr_inputs.butterfly_inputs()
+    xd = torch.from_numpy(bi.x).to(DEV)
+    co = hr.butterfly_coeffs(torch.from_numpy(bi.angles).to(DEV), False)
+    pd = torch.from_numpy(bi.perm).to(DEV)
+    rows = _sample(bi.rows, 64, seed=44)
+    rd = torch.from_numpy(rows).to(DEV)
+    y64 = oracle.butterfly.butterfly(bi.x[rows], bi.angles, bi.perm)
+    y = hr.butterfly_apply(xd, co, False, pd)
+    check_rotated(y[rd].cpu().numpy(), y64)
+    del y
+    none, codes, scales = hr.butterfly_apply(xd, co, False, pd, want_y=False, group=64)
+    assert none is None
+    check_quant(codes.cpu().numpy()[rows], scales.cpu().numpy()[rows], y64, 64, "f16")
+
+
+def test_dequant_65536x2048(rht_full):
+    """Dequantization of the headline codes at full size (grid-stride loop
+    over 33.5 M quads), bit-exact on sampled rows."""
+    hr = _hr()
+    inp, xd, dd = rht_full
+    codes, scales = hr.rotate_quant_int4(xd, 128, dd)
+    out = hr.dequant_int4(codes, scales, 128)
+    rows = _sample(inp.rows, 256, seed=12)
+    q = oracle.quant.unpack_int4(codes.cpu().numpy()[rows])
+    ref = oracle.quant.dequant(q, scales.cpu().numpy()[rows], 128)
+    assert np.array_equal(out.cpu().numpy()[rows].view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("M", [4096, 16])
 def test_gemm_4096(M):
     hr = _hr()

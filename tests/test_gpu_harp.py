@@ -131,3 +131,7 @@ def test_harp_4096x5120_sampled():
     ri = torch.from_numpy(rows).to(DEV)
     check_rotated(y[ri].cpu().numpy(), y64)
     check_quant(codes[ri].cpu().numpy(), scales[ri].cpu().numpy(), y64, 128, "f16")
+    # the codes-only call the bench times computes the same codes and scales
+    none, codes2, scales2 = hr.harp_apply(_t(hi.x), hi.radices, blk, want_y=False, group=128)
+    assert none is None
+    assert torch.equal(codes2, codes) and torch.equal(scales2, scales)
