@@ -1,8 +1,8 @@
-// Randomized Hadamard transform of bf16 rows of 2048 elements, fused with
-// int4 or int8 quantization (or an fp32 store), with the 128-point factor of
-// the transform on bf16 matrix cores.
+// Randomized Hadamard transform of bf16 rows of 2048 (or 4096) elements, fused
+// with int4 or int8 quantization (or an fp32 store), with the 128-point factor
+// of the transform on bf16 matrix cores.
 //
-// What is computed: y = H_2048 (d * x) / sqrt(2048) per row, Sylvester order
+// What is computed: y = H_n (d * x) / sqrt(n) per row, Sylvester order
 // ("Experiment -- Hadamard rotation for int4 (W4A4) accuracy", Hypothesis and
 // Method; "Llama-3.2-1B-Instruct-HadamardSpin-4bits", How it Works), then
 // groups of G consecutive outputs quantized with scale absmax / 7 (same
@@ -10,7 +10,10 @@
 // (same page, the W4A8 rows of Results).
 //
 // The transform is the matrix-core routine of mfma2048.h (H_128 on
-// v_mfma_f32_16x16x32_bf16, H_16 as DPP butterflies).
+// v_mfma_f32_16x16x32_bf16, H_16 as DPP butterflies).  A row of n = 4096 is
+// two 2048-point chunks in the same wave: H_4096 = H_2 kron H_2048, and the
+// two chunk transforms leave each output position in the same lane, so the
+// H_2 stage is a lane-local sum and difference.
 //
 //   Staging: each wave streams its rows through two 4 KB LDS stages filled by
 //     global_load_lds_dwordx4 (two rows in flight per wave without holding
@@ -27,57 +30,86 @@ namespace hr {
 
 constexpr int kMfmaBlocksPerCu = 2;
 
-template <int G, bool SCALE_F16, bool OUT_F32, int BITS>
+// 16-byte global -> LDS copy (the builtin sits in a device function: used
+// directly in a kernel template it can cost the instance its host stub)
+__device__ __forceinline__ void mfma_lds_load16(const void* gp, void* lp) {
+  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+}
+
+template <int G, bool SCALE_F16, bool OUT_F32, int BITS, int CH = 1>
 __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ signs, int64_t rows,
     float* __restrict__ yout, uint8_t* __restrict__ codes, void* __restrict__ scales, float norm) {
-  constexpr int N = 2048;
+  static_assert(CH == 1 || CH == 2, "rows of one or two 2048-point chunks");
+  constexpr int P = 2048;          // chunk
+  constexpr int N = CH * P;        // row
   const int lane = threadIdx.x & 63;
   const int wib = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wib;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  Mfma2048 M;
-  mfma2048_init(M, lane, signs);
-  const int g = M.g, a4 = M.a4;
-  const float tau = M.tau;
+  Mfma2048 M[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) mfma2048_init(M[c], lane, signs ? signs + c * P : nullptr);
+  const int g = M[0].g, a4 = M[0].a4;
+  const float tau = M[0].tau;
 
-  // LDS of this wave: two row stages (256 slots of 16 bytes) and one row of codes
-  __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][2][256];
+  // LDS of this wave: two row stages (256 slots of 16 bytes per chunk) and
+  // one chunk of codes
+  __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][2][CH * 256];
   __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][BITS == 8 ? 128 : 64];
   // fp32 output: this wave's 8 KB output row, staged so it leaves as 1 KB stores
   __shared__ __attribute__((aligned(16))) f32x4 out_lds[OUT_F32 ? 4 : 1][OUT_F32 ? 512 : 1];
   // element offset of this lane's piece within a row, per load j: + 32 j
   const int lane_src = 128 * (lane & 15) + 8 * (lane >> 4);
   auto issue = [&](int64_t row, int st) {
-    const uint16_t* base = x + row * N + lane_src;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds(base + 32 * j, &stage_lds[wib][st][64 * j], 16, 0, 0);
+    for (int c = 0; c < CH; ++c) {
+      const uint16_t* base = x + row * N + c * P + lane_src;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        mfma_lds_load16(base + 32 * j, &stage_lds[wib][st][256 * c + 64 * j]);
+    }
   };
   // B operands of one row from stage st: lane (q, g) takes slot 64 s + 16 g +
-  // A(q) for K-step s.  One asm block waits for the stage (at most 4 younger
-  // vector-memory ops, the other stage's loads, may still be pending; loads
-  // complete in order) and for its own results.
+  // A(q) of each chunk for K-step s.  One asm block waits for the stage (at
+  // most 4 CH younger vector-memory ops, the other stage's loads, may still be
+  // pending; loads complete in order) and for its own results.
   const uint32_t rd_lane = 16u * (uint32_t)(16 * g + a4);
-  auto read_stage = [&](int st, bool next_pending, u32x4 (&b)[4]) {
+  auto read_stage = [&](int st, bool next_pending, u32x4 (&b)[CH][4]) {
     const uint32_t addr = (uint32_t)(uintptr_t)&stage_lds[wib][st][0] + rd_lane;
 #define HR_DSR4(WAIT)                                                                    \
     asm volatile(WAIT "\n\t"                                                             \
                  "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"             \
                  "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t" \
                  "s_waitcnt lgkmcnt(0)"                                                  \
-                 : "=v"(b[0]), "=v"(b[1]), "=v"(b[2]), "=v"(b[3])                         \
+                 : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3])             \
                  : "v"(addr)                                                             \
                  : "memory")
-    if (next_pending) HR_DSR4("s_waitcnt vmcnt(4)");
-    else HR_DSR4("s_waitcnt vmcnt(0)");
+#define HR_DSR8(WAIT)                                                                    \
+    asm volatile(WAIT "\n\t"                                                             \
+                 "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"             \
+                 "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t" \
+                 "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t" \
+                 "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t" \
+                 "s_waitcnt lgkmcnt(0)"                                                  \
+                 : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3]),            \
+                   "=v"(b[CH - 1][0]), "=v"(b[CH - 1][1]), "=v"(b[CH - 1][2]), "=v"(b[CH - 1][3]) \
+                 : "v"(addr)                                                             \
+                 : "memory")
+    if (CH == 1) {
+      if (next_pending) HR_DSR4("s_waitcnt vmcnt(4)");
+      else HR_DSR4("s_waitcnt vmcnt(0)");
+    } else {
+      if (next_pending) HR_DSR8("s_waitcnt vmcnt(8)");
+      else HR_DSR8("s_waitcnt vmcnt(0)");
+    }
 #undef HR_DSR4
+#undef HR_DSR8
   };
 
-  auto process = [&](int64_t row, const u32x4 (&b)[4]) {
-    f32x4 acc[8];
-    mfma2048_transform(M, b, acc);
-    // lane now holds tau * Y[a4][c], c = v + 4 T0 + 8 g + 32 T1 + 64 T2
+  // outputs of chunk ch of a row: acc[T][v] = tau * Y[a4][c] of the chunk,
+  // c = v + 4 T0 + 8 g + 32 T1 + 64 T2
+  auto emit = [&](int64_t row, int ch, const f32x4 (&acc)[8]) {
     if (OUT_F32) {
       // 16-byte slot 32 a + s of the row (s = 8 m + 2 g + h) sits at 32 a +
       // (s ^ a): the lanes of a write phase, which differ in a, then hit
@@ -91,7 +123,7 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
         ol[32 * a4 + ((8 * m + 2 * g + 1) ^ a4)] = (f32x4){hi[0] * ym, hi[1] * ym, hi[2] * ym, hi[3] * ym};
       }
       __builtin_amdgcn_wave_barrier();
-      f32x4* dst = reinterpret_cast<f32x4*>(yout + row * N);
+      f32x4* dst = reinterpret_cast<f32x4*>(yout + row * N + ch * P);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int sl = 64 * i + lane, a = sl >> 5;
@@ -138,10 +170,11 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
     }
     {
       int64_t si = -1;
-      if (G == 32) si = row * 64 + 4 * a4 + g;
-      else if (G == 64) si = g < 2 ? row * 32 + 2 * a4 + g : -1;
-      else if (G == 128) si = g == 0 ? row * 16 + a4 : -1;
-      else si = (g == 0 && (a4 & 1) == 0) ? row * 8 + (a4 >> 1) : -1;
+      const int64_t s0 = row * (N / G) + ch * (P / G);   // the chunk's first group
+      if (G == 32) si = s0 + 4 * a4 + g;
+      else if (G == 64) si = g < 2 ? s0 + 2 * a4 + g : -1;
+      else if (G == 128) si = g == 0 ? s0 + a4 : -1;
+      else si = (g == 0 && (a4 & 1) == 0) ? s0 + (a4 >> 1) : -1;
       if (si >= 0) {
         if (SCALE_F16) reinterpret_cast<_Float16*>(scales)[si] = (_Float16)s_own;
         else reinterpret_cast<float*>(scales)[si] = s_own;
@@ -183,23 +216,43 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
       // lane i stores bytes 16 i .. 16 i + 15 of the row: block (i >> 2, i & 3)
       const int ra = lane >> 2, rm = lane & 3;
       const u32x4 out = cl[4 * ra + (rm ^ ((ra >> 2) & 3))];
-      __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * (N / 2)) + lane);
+      __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * (N / 2) + ch * (P / 2)) + lane);
     } else {
       // 16-byte block b = 8 a + k of the row sits at 8 a + (k ^ (a >> 1))
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int b = 64 * h + lane, ra = b >> 3;
         const u32x4 out = cl[8 * ra + ((b & 7) ^ (ra >> 1))];
-        __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * N) + b);
+        __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * N + ch * P) + b);
       }
     }
+  };
+
+  auto process = [&](int64_t row, const u32x4 (&b)[CH][4]) {
+    f32x4 acc[8];
+    mfma2048_transform(M[0], b[0], acc);
+    if (CH == 1) {
+      emit(row, 0, acc);
+      return;
+    }
+    f32x4 acc1[8], dif[8];
+    mfma2048_transform(M[CH - 1], b[CH - 1], acc1);
+    // H_2 across the chunks: the same lane holds the same position (and the
+    // same sign tau) of both
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      dif[t] = acc[t] - acc1[t];
+      acc[t] = acc[t] + acc1[t];
+    }
+    emit(row, 0, acc);
+    emit(row, 1, dif);
   };
 
   int64_t row = wave;
   if (row < rows) issue(row, 0);
   if (row + nwaves < rows) issue(row + nwaves, 1);
   for (int st = 0; row < rows; row += nwaves, st ^= 1) {
-    u32x4 b[4];
+    u32x4 b[CH][4];
     read_stage(st, row + nwaves < rows, b);
     if (row + 2 * nwaves < rows) issue(row + 2 * nwaves, st);
     process(row, b);
@@ -211,17 +264,25 @@ static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
   int64_t blocks = (a.rows + 3) / 4;              // 4 waves per block, one row per wave
   const int64_t cap = 256 * kMfmaBlocksPerCu;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS>), dim3((unsigned)blocks), dim3(256),
-                     0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
-                     a.scales, norm);
+  if (a.p == 4096)
+    hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS, 2>), dim3((unsigned)blocks),
+                       dim3(256), 0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
+                       a.scales, norm);
+  else
+    hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS>), dim3((unsigned)blocks),
+                       dim3(256), 0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
+                       a.scales, norm);
 }
 
-// bf16 rows of n = 2048 (m = 1): fp32 output or fused int4 / int8
-// quantization.  Returns
-// false when the case belongs to another kernel.
+// bf16 rows of n = 2048 or 4096 (m = 1): fp32 output or fused int4 / int8
+// quantization.  Returns false when the case belongs to another kernel.
 bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s) {
-  if (!a.x_bf16 || a.p != 2048 || a.m != 1) return false;
-  const float norm = (float)(1.0 / sqrt(2048.0));
+  if (!a.x_bf16 || (a.p != 2048 && a.p != 4096) || a.m != 1) return false;
+  // n = 4096 with fewer rows than one resident wave per row: the mixed-radix
+  // kernel, which spreads each row over eight waves, has the lower latency
+  // (16 rows: 3.3 us against 5.0 us)
+  if (a.p == 4096 && a.rows < 256 * kMfmaBlocksPerCu * 4) return false;
+  const float norm = (float)(1.0 / sqrt((double)a.p));
   if (a.y && !a.codes) {
     launch_mfma<0, false, true>(a, norm, s);
     return true;

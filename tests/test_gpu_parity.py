@@ -107,6 +107,33 @@ def test_rotate_quant(n, group, scale_mode):
     check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, scale_mode)
 
 
+@pytest.mark.parametrize("group,scale_mode,bits", [(128, "f16", 4), (32, "f32", 4), (64, "f16", 4),
+                                                  (256, "f32", 4), (128, "f16", 8), (32, "f32", 8)])
+def test_rotate_quant_4096_wave_per_row(group, scale_mode, bits):
+    """n = 4096 with enough rows for the one-wave-per-row kernel (two
+    2048-point chunks per wave, H_2 across them); some waves take two rows."""
+    hr = _hr()
+    rows, n = 2100, 4096
+    x, d = _bf16_rows(rows, n, seed=4096 + group + bits)
+    sd = torch.float16 if scale_mode == "f16" else torch.float32
+    fn = hr.rotate_quant_int4 if bits == 4 else hr.rotate_quant_int8
+    codes, scales = fn(x.to(DEV), group, torch.from_numpy(d).to(DEV), scale_dtype=sd)
+    sample = np.unique(np.concatenate([np.random.default_rng(group).choice(rows, 40, replace=False),
+                                       [0, 2047, 2048, rows - 1]]))
+    y64 = oracle.hadamard.rht(x[sample].float().numpy(), d)
+    check_quant(codes.cpu().numpy()[sample], scales.cpu().numpy()[sample], y64, group, scale_mode, bits)
+
+
+def test_rotate_4096_wave_per_row_fp32_out():
+    hr = _hr()
+    rows, n = 2100, 4096
+    x, d = _bf16_rows(rows, n, seed=4097)
+    y = hr.rotate(x.to(DEV), torch.from_numpy(d).to(DEV)).cpu().numpy()
+    sample = np.unique(np.concatenate([np.random.default_rng(5).choice(rows, 40, replace=False),
+                                       [0, 2047, 2048, rows - 1]]))
+    check_rotated(y[sample], oracle.hadamard.rht(x[sample].float().numpy(), d))
+
+
 def test_rotate_quant_fp32_input_and_zero_rows():
     hr = _hr()
     n, group = 2048, 128
