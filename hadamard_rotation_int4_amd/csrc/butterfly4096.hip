@@ -17,7 +17,9 @@
 // index bits 3k..3k+2 take all 8 values, the other 9 bits being the thread
 // index; between passes the row goes through LDS.  Because a thread owns the
 // same pairs in every row, its 12 x 4 pairs' coefficients stay in registers
-// for the kernel's lifetime.  The LDS index is padded by 8 floats every 64
+// for the kernel's lifetime.  Passes 1 and 2 exchange elements only within a
+// wave, so of the four exchanges per row only pass 3 and the permutation take
+// a workgroup barrier.  The LDS index is padded by 8 floats every 64
 // (p = i + 8 * (i >> 6)) so that the one strided pass (k = 1) is bank-conflict
 // free; the other passes access consecutive elements.
 #include "hr_internal.h"
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
     const float2* __restrict__ coeffs, const int* __restrict__ perm,
     uint8_t* __restrict__ codes, void* __restrict__ scales) {
   constexpr int N = kBfN, HALF = N / 2;
-  __shared__ __attribute__((aligned(16))) float lds[2][kBfLds];
+  __shared__ __attribute__((aligned(16))) float lds[3][kBfLds];
   // the ring only where the row's fp32 output makes the kernel memory-bound;
   // with codes only, its extra LDS traffic costs more than it hides
   constexpr bool RING = OUT_Y;
@@ -182,58 +184,72 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
       // pass 0: stages 0, 1, 2 on elements 8t .. 8t+7
 #pragma unroll
       for (int b = 0; b < 3; ++b) bf_stage<PRECOND, false>(v, cf[b], b);
-      int buf = 0;
+      // Passes 1 and 2 move elements only within a wave (wave w writes and
+      // reads elements 512 w .. 512 w + 511), and a wave's LDS accesses take
+      // effect in issue order, so they need no workgroup barrier.  Pass 3 and
+      // the gather cross waves.  Buffers: passes 1 and 3 in 0, pass 2 in 1,
+      // the gather in 2, so that every access by one wave to a region another
+      // wave used is separated by one of the two barriers.
 #pragma unroll
       for (int k = 1; k < 4; ++k) {
+        float* bk = lds[k == 2 ? 1 : 0];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, k - 1, r))] = v[r];
-        bf_barrier();
+        for (int r = 0; r < 8; ++r) bk[bf_pad(bf_idx(t, k - 1, r))] = v[r];
+        if (k < 3) asm volatile("" ::: "memory");    // keep the reads after the writes
+        else bf_barrier();
 #pragma unroll
-        for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, k, r))];
+        for (int r = 0; r < 8; ++r) v[r] = bk[bf_pad(bf_idx(t, k, r))];
 #pragma unroll
         for (int b = 0; b < 3; ++b) bf_stage<PRECOND, false>(v, cf[3 * k + b], b);
-        buf ^= 1;
       }
       // gather: out[8t + r] = z[perm[8t + r]]
+      float* bg = lds[2];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, 3, r))] = v[r];
+      for (int r = 0; r < 8; ++r) bg[bf_pad(bf_idx(t, 3, r))] = v[r];
       bf_barrier();
       if (perm) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(pm[r])];
+        for (int r = 0; r < 8; ++r) v[r] = bg[bf_pad(pm[r])];
       } else {
         // identity: elements 8t .. 8t+7 are 8 consecutive padded slots, read
         // as two 16-byte loads (eight scalar loads at a stride of 8 conflict)
-        const f32x4* src = reinterpret_cast<const f32x4*>(&lds[buf][bf_pad(8 * t)]);
+        const f32x4* src = reinterpret_cast<const f32x4*>(&bg[bf_pad(8 * t)]);
         const f32x4 u0 = src[0], u1 = src[1];
         v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
         v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
       }
     } else {
-      // scatter z[perm[i]] = x[i], then the transposed stages in reverse order
+      // scatter z[perm[i]] = x[i], then the transposed stages in reverse
+      // order.  As in the forward direction only the scatter and the pass-3
+      // exchange cross waves: the scatter goes to buffer 2, pass 3 writes
+      // buffer 0, pass 2 buffer 1 and pass 1 buffer 0 again, with workgroup
+      // barriers after the first two only.
+      float* bs = lds[2];
       if (perm) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) lds[0][bf_pad(pm[r])] = v[r];
+        for (int r = 0; r < 8; ++r) bs[bf_pad(pm[r])] = v[r];
       } else {
-        f32x4* dst = reinterpret_cast<f32x4*>(&lds[0][bf_pad(8 * t)]);
+        f32x4* dst = reinterpret_cast<f32x4*>(&bs[bf_pad(8 * t)]);
         dst[0] = (f32x4){v[0], v[1], v[2], v[3]};
         dst[1] = (f32x4){v[4], v[5], v[6], v[7]};
       }
       bf_barrier();
-      int buf = 0;
+      float* src = bs;
 #pragma unroll
       for (int k = 3; k >= 1; --k) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, k, r))];
+        for (int r = 0; r < 8; ++r) v[r] = src[bf_pad(bf_idx(t, k, r))];
 #pragma unroll
         for (int b = 2; b >= 0; --b) bf_stage<PRECOND, true>(v, cf[3 * k + b], b);
-        buf ^= 1;
+        float* dstb = lds[k == 2 ? 1 : 0];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) lds[buf][bf_pad(bf_idx(t, k, r))] = v[r];
-        bf_barrier();
+        for (int r = 0; r < 8; ++r) dstb[bf_pad(bf_idx(t, k, r))] = v[r];
+        if (k == 3) bf_barrier();
+        else asm volatile("" ::: "memory");      // keep the reads after the writes
+        src = dstb;
       }
 #pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = lds[buf][bf_pad(bf_idx(t, 0, r))];
+      for (int r = 0; r < 8; ++r) v[r] = src[bf_pad(bf_idx(t, 0, r))];
 #pragma unroll
       for (int b = 2; b >= 0; --b) bf_stage<PRECOND, true>(v, cf[b], b);
     }
