@@ -33,7 +33,7 @@ PROFILES = os.path.join(HERE, "profiles")
 CSRC = os.path.join(HERE, "hadamard_rotation_int4_amd", "csrc")
 # sources that make up the headline kernel (its counters go stale when they change)
 MAIN_KERNEL_SOURCES = ("rht2048_mfma.hip", "mfma2048.h", "fwht2048.h", "hr_device.h", "hr_internal.h")
-MAIN_KERNEL_NAME = "rht2048_mfma_kernel<128, true, false, 4>"
+MAIN_KERNEL_NAME = "rht2048_mfma_kernel<128, true, false, 4, 1>"
 TRAFFIC_FILE = os.path.join(PROFILES, "rht_quant_bf16_65536x2048_g128.traffic.json")
 COPY_BYTES = 512 * 1024 * 1024       # calibration copy: reads and writes this many bytes
 
@@ -469,8 +469,8 @@ def summarize_profile(d):
         f.write("\n".join(lines) + "\n")
     fetch = _read_csv(os.path.join(d, "fetch", "**", "*counter_collection.csv"))
     write = _read_csv(os.path.join(d, "write", "**", "*counter_collection.csv"))
-    kf, nk = _counter_per_dispatch(fetch, "rht2048_mfma_kernel<128, true, false, 4>", "FETCH_SIZE")
-    kw, _ = _counter_per_dispatch(write, "rht2048_mfma_kernel<128, true, false, 4>", "WRITE_SIZE")
+    kf, nk = _counter_per_dispatch(fetch, MAIN_KERNEL_NAME, "FETCH_SIZE")
+    kw, _ = _counter_per_dispatch(write, MAIN_KERNEL_NAME, "WRITE_SIZE")
     cf = cw = None
     nc = 0
     copy_kernel = None
