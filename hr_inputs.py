@@ -250,6 +250,35 @@ def gemm_w4a8_inputs(M: int = 4096, N: int = 4096, K: int = 4096, group: int = 1
     return GemmW4A8Inputs(a_codes, a_scales, w_codes, w_scales, M, N, K, group)
 
 
+SEED_GEMM8 = 7
+
+
+@dataclass
+class GemmI8Inputs:
+    a_codes: np.ndarray    # int8 [M][K], one code per element
+    a_scales: np.ndarray   # fp16 [M][K/G]
+    w_codes: np.ndarray    # int8 [N][K]
+    w_scales: np.ndarray   # fp16 [N][K/G]
+    M: int
+    N: int
+    K: int
+    group: int
+
+
+def gemm_i8_inputs(M: int = 4096, N: int = 4096, K: int = 4096, group: int = 128,
+                   seed: int = SEED_GEMM8, code_max: int = 7) -> GemmI8Inputs:
+    """GEMM operands with the codes held one per byte.  code_max = 7: the W4A4
+    workload (codes uniform in -7..7, fp16 scales U(0.001, 0.05)) for an int8
+    MAC; code_max = 127: W8A8.  Draw order: W codes, W scales, A codes, A
+    scales."""
+    rng = _rng(seed)
+    w_codes = rng.integers(-code_max, code_max + 1, size=(N, K)).astype(np.int8)
+    w_scales = random_scales_f16(rng, N, K // group)
+    a_codes = rng.integers(-code_max, code_max + 1, size=(M, K)).astype(np.int8)
+    a_scales = random_scales_f16(rng, M, K // group)
+    return GemmI8Inputs(a_codes, a_scales, w_codes, w_scales, M, N, K, group)
+
+
 @dataclass
 class ProbeInputs:
     a: np.ndarray          # fp32 [M][K] activations with outlier channels

@@ -16,7 +16,8 @@ The integer sums are computed with an fp64 matrix product, which is exact here
 
 W4A8 (same page, Method and Results: the "W4A8 (act8/wt4)" rows, int8
 activations against int4 weights): the same two formulas with A held as one
-int8 code per element instead of packed nibbles.
+int8 code per element instead of packed nibbles.  W8A8 (the W8A8 rows): both
+operands held that way.
 """
 from __future__ import annotations
 
@@ -66,6 +67,22 @@ def w4a8_gemm(a_codes, a_scales, w_packed, w_scales, group: int, rows=None,
     if a.dtype != np.int8:
         raise ValueError("a_codes must be int8")
     acc = _group_sums(a, unpack_int4(w_packed), group, rows)
+    return _scale_sum(acc, a_scales, w_scales, rows, return_sums)
+
+
+def w8a8_gemm(a_codes, a_scales, w_codes, w_scales, group: int, rows=None,
+              return_sums: bool = False):
+    """Both operands held one int8 code per element: A [M][K], W [N][K].
+
+    Covers the W8A8 rows of the experiment page's Results (int8 activations
+    and weights) and the W4A4 GEMM with its int4 codes held in int8 for an
+    int8 MAC; the sums and the scale fusion are those of w4a4_gemm.  Returns
+    as w4a4_gemm."""
+    a = np.asarray(a_codes)
+    w = np.asarray(w_codes)
+    if a.dtype != np.int8 or w.dtype != np.int8:
+        raise ValueError("a_codes and w_codes must be int8")
+    acc = _group_sums(a, w, group, rows)
     return _scale_sum(acc, a_scales, w_scales, rows, return_sums)
 
 

@@ -194,3 +194,70 @@ def test_w4a8_inputs_ranges():
     assert w.min() >= -7 and w.max() <= 7
     g4 = hr_inputs.gemm_inputs(M=8, N=16, K=512)
     assert np.array_equal(gi.w_codes, g4.w_codes) and np.array_equal(gi.w_scales, g4.w_scales)
+
+
+# ------------------------------------------------------------------ W8A8
+
+def test_w8a8_brute_force_tiny():
+    """Loops over every product against the matrix form, both operands int8."""
+    rng = np.random.default_rng(13)
+    M, N, K, G = 3, 4, 32, 16
+    a = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    w = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.0001, 0.005, size=(M, K // G)).astype(np.float16)
+    sw = rng.uniform(0.0001, 0.005, size=(N, K // G)).astype(np.float16)
+    c, acc, bound = oracle.gemm.w8a8_gemm(a, sa, w, sw, G, return_sums=True)
+    cb, accb = _brute_gemm(a, sa, w, sw, G)
+    assert np.array_equal(acc, accb)
+    np.testing.assert_allclose(c, cb, rtol=1e-6, atol=1e-12)
+    assert np.all(bound >= np.abs(c) * (1 - 1e-6))
+
+
+def test_w8a8_extreme_codes_exact():
+    """-128 * -128 over a whole 256-code group: the largest group sum."""
+    K, G = 512, 256
+    a = np.full((2, K), -128, dtype=np.int8)
+    a[1, :] = 127
+    w = np.full((3, K), -128, dtype=np.int8)
+    ones_a = np.ones((2, K // G), dtype=np.float16)
+    ones_w = np.ones((3, K // G), dtype=np.float16)
+    c, acc, _ = oracle.gemm.w8a8_gemm(a, ones_a, w, ones_w, G, return_sums=True)
+    assert acc[0, 0, 0] == 128 * 128 * 256 and acc[1, 2, 1] == -127 * 128 * 256
+    assert c[0, 1] == 2 * 128 * 128 * 256
+
+
+def test_w8a8_on_int4_codes_equals_w4a4():
+    """int4 codes held in int8 give exactly the packed W4A4 result."""
+    gi = hr_inputs.gemm_i8_inputs(M=5, N=32, K=512, group=128, seed=23)
+    c8, acc8, _ = oracle.gemm.w8a8_gemm(gi.a_codes, gi.a_scales, gi.w_codes, gi.w_scales, 128,
+                                        return_sums=True)
+    c4, acc4, _ = oracle.gemm.w4a4_gemm(oracle.quant.pack_int4(gi.a_codes), gi.a_scales,
+                                        oracle.quant.pack_int4(gi.w_codes), gi.w_scales, 128,
+                                        return_sums=True)
+    assert np.array_equal(acc4, acc8) and np.array_equal(c4, c8)
+
+
+def test_w8a8_scale_linearity():
+    """Doubling one row's A scales doubles that row of C, exactly (powers of two)."""
+    gi = hr_inputs.gemm_i8_inputs(M=4, N=16, K=256, group=64, seed=24, code_max=127)
+    c = oracle.gemm.w8a8_gemm(gi.a_codes, gi.a_scales, gi.w_codes, gi.w_scales, 64)
+    sa = gi.a_scales.copy()
+    sa[2] *= np.float16(2)
+    c2 = oracle.gemm.w8a8_gemm(gi.a_codes, sa, gi.w_codes, gi.w_scales, 64)
+    assert np.array_equal(c2[2], 2 * c[2]) and np.array_equal(np.delete(c2, 2, 0), np.delete(c, 2, 0))
+
+
+def test_w8a8_rejects_packed_operands():
+    gi = hr_inputs.gemm_inputs(M=2, N=4, K=256)
+    a8 = oracle.quant.unpack_int4(gi.a_codes)
+    with pytest.raises(ValueError):
+        oracle.gemm.w8a8_gemm(a8, gi.a_scales, gi.w_codes, gi.w_scales, 128)
+
+
+def test_gemm_i8_inputs_ranges():
+    g4 = hr_inputs.gemm_i8_inputs(M=8, N=16, K=512)
+    assert g4.a_codes.dtype == np.int8 and g4.w_codes.dtype == np.int8
+    assert g4.a_codes.min() >= -7 and g4.a_codes.max() <= 7 and g4.w_codes.min() >= -7
+    assert g4.a_scales.min() >= 0.001 and g4.a_scales.max() <= 0.05
+    g8 = hr_inputs.gemm_i8_inputs(M=8, N=16, K=512, code_max=127)
+    assert g8.a_codes.min() >= -127 and g8.w_codes.max() <= 127 and g8.a_codes.min() < -7
