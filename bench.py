@@ -351,6 +351,19 @@ def main(argv=None):
                 "GB/s": byts / msg / 1e6, "ops": ops, "bytes": byts,
                 "timing": "eager launches" if M > 16 else "HIP graph of 20 launches, replayed"}
 
+        # W8A8 GEMM: the W4A4 workload with its codes held one per byte
+        g8 = hr_inputs.gemm_i8_inputs(M=4096)
+        t = lambda a: torch.from_numpy(a).to(dev)  # noqa: E731
+        ad, sad, wd, swd = t(g8.a_codes), t(g8.a_scales), t(g8.w_codes), t(g8.w_scales)
+        cg = torch.empty((4096, 4096), dtype=torch.float32, device=dev)
+        msg = _timed(lambda i: hr.w8a8_gemm(ad, sad, wd, swd, 128, out=cg), args.steps, args.warmup)
+        ops = 2 * 4096 ** 3
+        byts = 2 * 4096 * 4096 + 2 * 4096 * 32 * 2 + 4096 * 4096 * 4
+        kernels["w8a8_gemm_4096x4096x4096_g128"] = {
+            "ms": msg, "TOPS": ops / msg / 1e9, "frac_int8_peak": ops / msg / 1e9 / INT8_PEAK_TOPS,
+            "GB/s": byts / msg / 1e6, "ops": ops, "bytes": byts, "timing": "eager launches",
+            "codes": "int4 values held in int8 (uniform -7..7)"}
+
     out = {
         "metric": METRIC,
         "value": round(gbs, 2),

@@ -42,6 +42,7 @@ SYMBOLS = {
     "hr_dequant_int4": (_i32, [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp]),
     "hr_w4a4_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "hr_w4a8_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "hr_w8a8_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
 }
 
 
@@ -273,4 +274,25 @@ def w4a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tens
     _check(lib.hr_w4a8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
                             _dtype_code(a_scales.dtype), M, N, K, group, _ptr(c), _ptr(acc),
                             _stream(a_codes.device)), "hr_w4a8_gemm")
+    return (c, acc) if group_acc else c
+
+
+def w8a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
+              w_scales: torch.Tensor, group: int, out: torch.Tensor | None = None,
+              group_acc: bool = False):
+    """C = A W^T with both operands held one int8 code per element:
+    a_codes [M][K], w_codes [N][K] (hr_w8a8_gemm).  Returns as w4a4_gemm."""
+    if a_codes.dtype != torch.int8 or w_codes.dtype != torch.int8:
+        raise TypeError("a_codes and w_codes must be int8 [M][K] and [N][K]")
+    M, K = a_codes.shape
+    N = int(w_codes.shape[0])
+    if a_scales.dtype != w_scales.dtype:
+        raise TypeError("a_scales and w_scales must share a dtype")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    acc = None
+    if group_acc:
+        acc = torch.empty((M, N, K // group), dtype=torch.int32, device=a_codes.device)
+    _check(lib.hr_w8a8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
+                            _dtype_code(a_scales.dtype), M, N, K, group, _ptr(c), _ptr(acc),
+                            _stream(a_codes.device)), "hr_w8a8_gemm")
     return (c, acc) if group_acc else c

@@ -318,8 +318,8 @@ int32_t hr_dequant_int4(const uint8_t* codes, const void* scales, int32_t scale_
                                      static_cast<hipStream_t>(stream)), fn);
 }
 
-// Shared body of hr_w4a4_gemm and hr_w4a8_gemm.
-static int32_t gemm(const char* fn, int a_int8, const uint8_t* a_codes, const void* a_scales,
+// Shared body of hr_w4a4_gemm, hr_w4a8_gemm and hr_w8a8_gemm.
+static int32_t gemm(const char* fn, int a_int8, int w_int8, const uint8_t* a_codes, const void* a_scales,
                     const uint8_t* w_codes, const void* w_scales, int32_t scale_dtype, int64_t M,
                     int64_t N, int64_t K, int32_t group, float* c, int32_t* group_acc,
                     void* stream) {
@@ -341,6 +341,7 @@ static int32_t gemm(const char* fn, int a_int8, const uint8_t* a_codes, const vo
   hr::GemmArgs a{};
   a.a = a_codes;
   a.a_int8 = a_int8;
+  a.w_int8 = w_int8;
   a.sa = a_scales;
   a.w = w_codes;
   a.sw = w_scales;
@@ -357,15 +358,23 @@ static int32_t gemm(const char* fn, int a_int8, const uint8_t* a_codes, const vo
 int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales, const uint8_t* w_codes,
                      const void* w_scales, int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
                      int32_t group, float* c, int32_t* group_acc, void* stream) {
-  return gemm("hr_w4a4_gemm", 0, a_codes, a_scales, w_codes, w_scales, scale_dtype, M, N, K, group,
+  return gemm("hr_w4a4_gemm", 0, 0, a_codes, a_scales, w_codes, w_scales, scale_dtype, M, N, K, group,
               c, group_acc, stream);
 }
 
 int32_t hr_w4a8_gemm(const int8_t* a_codes, const void* a_scales, const uint8_t* w_codes,
                      const void* w_scales, int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
                      int32_t group, float* c, int32_t* group_acc, void* stream) {
-  return gemm("hr_w4a8_gemm", 1, reinterpret_cast<const uint8_t*>(a_codes), a_scales, w_codes,
+  return gemm("hr_w4a8_gemm", 1, 0, reinterpret_cast<const uint8_t*>(a_codes), a_scales, w_codes,
               w_scales, scale_dtype, M, N, K, group, c, group_acc, stream);
+}
+
+int32_t hr_w8a8_gemm(const int8_t* a_codes, const void* a_scales, const int8_t* w_codes,
+                     const void* w_scales, int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
+                     int32_t group, float* c, int32_t* group_acc, void* stream) {
+  return gemm("hr_w8a8_gemm", 1, 1, reinterpret_cast<const uint8_t*>(a_codes), a_scales,
+              reinterpret_cast<const uint8_t*>(w_codes), w_scales, scale_dtype, M, N, K, group, c,
+              group_acc, stream);
 }
 
 }  // extern "C"

@@ -73,9 +73,11 @@ __global__ __launch_bounds__(256) void w4a4_gemm_simple_kernel(GemmArgs g) {
         if (m0 + r < g.M) qa = *reinterpret_cast<const uint32_t*>(g.a + (m0 + r) * (K / 2) + kb);
         a8 = unpack8(qa);
       }
-      const uint32_t qw = *reinterpret_cast<const uint32_t*>(g.w + (n0 + r) * (K / 2) + kb);
+      const uint64_t w8 =
+          g.w_int8 ? *reinterpret_cast<const uint64_t*>(g.w + (n0 + r) * K + (int64_t)gi * G + c * 8)
+                   : unpack8(*reinterpret_cast<const uint32_t*>(g.w + (n0 + r) * (K / 2) + kb));
       *reinterpret_cast<uint64_t*>(la + r * G + c * 8) = a8;
-      *reinterpret_cast<uint64_t*>(lw + r * G + c * 8) = unpack8(qw);
+      *reinterpret_cast<uint64_t*>(lw + r * G + c * 8) = w8;
     }
     __syncthreads();
     v4i acc[2][2];

@@ -363,6 +363,221 @@ __global__ __launch_bounds__(256, 2) void w4a4_gemm_tile_kernel(GemmArgs g) {
 }
 
 
+__device__ __forceinline__ void gemm_lds_load16(const void* gp, void* lp) {
+  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+}
+
+// W8A8 prefill kernel (M > 16): both operands one int8 code per element (the
+// W4A4 GEMM with its codes held in int8, or W8A8).  Tiling, waves, MFMAs, the
+// group epilogue and the scale ring are those of the packed kernel above;
+// the operands need no unpacking, so each stage's 16-byte pieces go from
+// memory straight into LDS with global_load_lds, without registers or vector
+// instructions.  LDS layout of one operand stage: tile row r keeps its SPR =
+// KS / 16 pieces at slots r SPR + (c ^ f(r)), f(r) = (r / (16 / SPR)) % SPR.
+// A load instruction fills 64 consecutive slots, i.e. whole rows read as
+// contiguous runs of KS bytes; the 16 lanes of a fragment-read phase (16
+// consecutive rows, one piece c) hit 16 different bank groups.  Codes are
+// used as they are: the int32 sums are the true group sums.
+template <int G, bool F16, bool WRITE_ACC>
+__global__ __launch_bounds__(256, 2) void w8a8_gemm_tile_kernel(GemmArgs g) {
+  constexpr int KS = G < 128 ? G : 128;   // codes per row and stage
+  constexpr int STEPS = KS / 32;          // MFMA K-steps per stage
+  constexpr int SPG = G / KS;             // stages per group (1 or 2)
+  constexpr int SPR = KS / 16;            // 16-byte pieces per row and stage
+  constexpr int RPF = 16 / SPR;           // f(r) = (r / RPF) % SPR
+  constexpr int OPB = 128 * KS;           // bytes of one operand stage
+  constexpr int LSC = 4 * OPB;            // byte offset of the scale ring
+  constexpr int SB = F16 ? 2 : 4;         // bytes per scale
+  constexpr int NDMA = 2 * 128 * SPR / 64;   // load instructions per stage
+  constexpr int DPW = NDMA / 4;              // ... per wave
+  __shared__ __attribute__((aligned(16))) char smem[4 * OPB + 3 * 1024];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, l32 = lane & 31;
+  const uint32_t hmask = h ? 0u : 0xFFFFFFFFu;
+  const int64_t m0 = (int64_t)blockIdx.y * kBM;
+  const int64_t n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t K = g.K;
+  const int ngroups = (int)(K / G);
+  const int nstages = (int)(K / KS);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  // this lane's source of load instruction j (slot block q = DPW wave + j of
+  // the stage: operand q / (NDMA / 2), its 64 slots from 64 (q % (NDMA / 2)));
+  // A rows past M read row 0 of the panel instead (a valid address, never
+  // stored).  Per stage the source advances by KS bytes.
+  // (32-bit offsets from the two panels' first rows keep the registers low)
+  const int8_t* pa = reinterpret_cast<const int8_t*>(g.a) + m0 * K;
+  const int8_t* pw = reinterpret_cast<const int8_t*>(g.w) + n0 * K;
+  int off[DPW];
+#pragma unroll
+  for (int j = 0; j < DPW; ++j) {
+    const int q = DPW * wave + j;
+    const int op = q / (NDMA / 2), sl = 64 * (q % (NDMA / 2)) + lane;
+    const int r = sl / SPR, c = (sl % SPR) ^ ((r / RPF) % SPR);
+    const int rr = op == 0 && m0 + r >= g.M ? 0 : r;
+    off[j] = rr * (int)K + 16 * c;
+  }
+  auto issue = [&](int s, int buf) {
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const int q = DPW * wave + j;
+      const int op = q / (NDMA / 2);
+      gemm_lds_load16((op == 0 ? pa : pw) + off[j] + s * KS,
+                      smem + buf * 2 * OPB + op * OPB + 64 * 16 * (q % (NDMA / 2)));
+    }
+  };
+  // scale row of this thread: threads 0-127 A rows, 128-255 W rows
+  const int64_t sr = tid < kBM ? (m0 + tid < g.M ? m0 + tid : m0) : n0 + tid - kBM;
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wave < 2 ? g.sa : g.sw), 0, 0x7FFFFFFF, 0x00020000);
+  const int svoff = (int)(sr * ngroups * SB);
+  auto load_scale = [&](int s) -> uint32_t {
+    const int gso = (s / SPG) * SB;
+    return F16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs_s, svoff, gso, 0)
+               : __builtin_amdgcn_raw_buffer_load_b32(rs_s, svoff, gso, 0);
+  };
+
+  // fragment read slots of K-step ks: piece 2 ks + h of row wm + l32 (+ 32 i)
+  const int xr = (l32 / RPF) % SPR;
+  int rd_a[STEPS], rd_b[STEPS];
+#pragma unroll
+  for (int ks = 0; ks < STEPS; ++ks) {
+    rd_a[ks] = ((wm + l32) * SPR + ((2 * ks + h) ^ xr)) * 16;
+    rd_b[ks] = OPB + ((wn + l32) * SPR + ((2 * ks + h) ^ xr)) * 16;
+  }
+
+  v16f c[2][2];
+  v16i acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      c[i][j] = (v16f){};
+      acc[i][j] = (v16i){};
+    }
+
+  auto mfma_half = [&](auto bufc, int i, bool zero_first, v4i (&bfr)[STEPS][2], bool read_b) {
+    const char* sb = smem + decltype(bufc)::value * 2 * OPB;
+#pragma unroll
+    for (int ks = 0; ks < STEPS; ++ks) {
+      const v4i af = *reinterpret_cast<const v4i*>(sb + rd_a[ks] + 32 * i * SPR * 16);
+      if (read_b) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bfr[ks][j] = *reinterpret_cast<const v4i*>(sb + rd_b[ks] + 32 * j * SPR * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = (zero_first && ks == 0)
+                        ? __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[ks][j], (v16i){}, 0, 0, 0)
+                        : __builtin_amdgcn_mfma_i32_32x32x32_i8(af, bfr[ks][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // group epilogue of tiles (i, 0) and (i, 1), as in the packed kernel
+  auto epilogue = [&](int i, int ring, int gi) {
+    const char* ls = smem + LSC + ring * 1024;
+    if (F16) {
+      const uint32_t ra = *reinterpret_cast<const uint32_t*>(ls + (wm + 32 * i + l32) * 4) & hmask;
+      const v4h sa = __builtin_bit_cast(v4h, (v2i){(int)ra, 0});
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t rw = *reinterpret_cast<const uint32_t*>(ls + (kBM + wn + 32 * j + l32) * 4) & hmask;
+        const v4h sw = __builtin_bit_cast(v4h, (v2i){(int)rw, 0});
+        const v16f p = __builtin_amdgcn_mfma_f32_32x32x8f16(sa, sw, (v16f){}, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c[i][j][v] = fmaf((float)acc[i][j][v], p[v], c[i][j][v]);
+      }
+    } else {
+      float sa[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 t4 = *reinterpret_cast<const uint4*>(ls + (wm + 32 * i + 8 * q + 4 * h) * 4);
+        sa[4 * q] = __uint_as_float(t4.x);
+        sa[4 * q + 1] = __uint_as_float(t4.y);
+        sa[4 * q + 2] = __uint_as_float(t4.z);
+        sa[4 * q + 3] = __uint_as_float(t4.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float sw = *reinterpret_cast<const float*>(ls + (kBM + wn + 32 * j + l32) * 4);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c[i][j][v] = fmaf((float)acc[i][j][v], sa[v] * sw, c[i][j][v]);
+      }
+    }
+    if (WRITE_ACC && gi >= 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int64_t col = n0 + wn + 32 * j + l32;
+          if (row < g.M) g.group_acc[(row * g.N + col) * ngroups + gi] = acc[i][j][v];
+        }
+    }
+  };
+
+  // one pipeline stage: the next stage's pieces and scale are requested
+  // first and land during the two halves; the barrier at the end (with its
+  // wait for them) makes them every wave's
+  auto stage = [&](int s, auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    constexpr int SUB = SPG == 1 ? 0 : B;
+    const int gi = s / SPG;
+    const int ring = s % 3;
+    // the last stage reloads itself (a valid address; the copy is never read)
+    issue(s + 1 < nstages ? s + 1 : s, B ^ 1);
+    const uint32_t psc = load_scale(s + 1 < nstages ? s + 1 : s);
+    v4i bfr[STEPS][2];
+    mfma_half(bufc, 0, SUB == 0, bfr, true);
+    if (SUB == 0) epilogue(1, ring == 0 ? 2 : ring - 1, gi - 1);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 16, 0);
+#pragma unroll
+    for (int q = 0; q < 2 * STEPS + 2; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_half(bufc, 1, SUB == 0, bfr, false);
+    if (SUB == SPG - 1) epilogue(0, ring, gi);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int q = 0; q < 2 * STEPS + 2; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    *reinterpret_cast<uint32_t*>(smem + LSC + (ring == 2 ? 0 : ring + 1) * 1024 + tid * 4) = psc;
+    __syncthreads();
+  };
+
+  // ring slot 2 stands for the group before the first one: zero scales make
+  // the lower tiles' first (empty) epilogue add nothing
+  *reinterpret_cast<uint32_t*>(smem + LSC + 2 * 1024 + tid * 4) = 0u;
+  issue(0, 0);
+  *reinterpret_cast<uint32_t*>(smem + LSC + tid * 4) = load_scale(0);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 <= nstages; s += 2) {
+    stage(s, IntC<0>{});
+    stage(s + 1, IntC<1>{});
+  }
+  if (s < nstages) stage(s, IntC<0>{});
+  epilogue(1, (nstages - 1) % 3, ngroups - 1);
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+      if (row < g.M) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) g.c[row * g.N + n0 + wn + 32 * j + l32] = c[i][j][v];
+      }
+    }
+}
+
 // M <= 16: each workgroup owns 16 output columns; its 16 waves split K.  The
 // unit of work is a 64-byte run of a packed row (128 codes), or two runs when
 // a group spans two (G = 256); wave w takes units [w U / 16, (w + 1) U / 16).
@@ -539,7 +754,32 @@ static void launch_da(const GemmArgs& a, hipStream_t s) {
 // The prefill kernel needs N % 128 == 0; the decode kernel takes every shape
 // the library accepts (N % 64 == 0, K a multiple of 256 and of the group).
 // Other shapes go to the simple kernel.
+template <int G, bool F16>
+static void launch_w8(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM));
+  if (a.group_acc)
+    hipLaunchKernelGGL((w8a8_gemm_tile_kernel<G, F16, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((w8a8_gemm_tile_kernel<G, F16, false>), grid, dim3(256), 0, s, a);
+}
+
+template <int G>
+static void launch_w8g(const GemmArgs& a, hipStream_t s) {
+  if (a.scale_f16) launch_w8<G, true>(a, s); else launch_w8<G, false>(a, s);
+}
+
 bool launch_gemm_mfma(const GemmArgs& a, hipStream_t s) {
+  if (a.w_int8) {
+    // int8 weights: the tile kernel for M > 16 and N % 128 == 0, else the
+    // simple kernel
+    if (!a.a_int8 || a.M <= 16 || a.N % kBN) return false;
+    switch (a.group) {
+      case 64: launch_w8g<64>(a, s); return true;
+      case 128: launch_w8g<128>(a, s); return true;
+      case 256: launch_w8g<256>(a, s); return true;
+      default: return false;
+    }
+  }
   const bool decode = a.M <= 16;
   if (!decode && a.N % kBN) return false;
   switch (a.group) {

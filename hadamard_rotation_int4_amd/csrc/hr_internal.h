@@ -40,7 +40,8 @@ struct ButterflyArgs {
 
 struct GemmArgs {
   const uint8_t* a;      // packed int4 [M][K/2], or int8 [M][K] when a_int8
-  int a_int8;            // 1: W4A8 (int8 activation codes)
+  int a_int8;            // 1: int8 activation codes [M][K] (W4A8, W8A8)
+  int w_int8;            // 1: int8 weight codes [N][K] (W8A8)
   const void* sa;
   const uint8_t* w;
   const void* sw;

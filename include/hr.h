@@ -54,7 +54,7 @@ typedef enum {
 } hr_dtype;
 
 /* ABI version of this header (bumped on any signature change). */
-#define HR_ABI_VERSION 2
+#define HR_ABI_VERSION 3
 int32_t hr_abi_version(void);
 
 /* Static description of a status code. */
@@ -322,6 +322,29 @@ int32_t hr_w4a4_gemm(const uint8_t* a_codes, const void* a_scales,
  */
 int32_t hr_w4a8_gemm(const int8_t* a_codes, const void* a_scales,
                      const uint8_t* w_codes, const void* w_scales,
+                     int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
+                     int32_t group, float* c, int32_t* group_acc, void* stream);
+
+/*
+ * hr_w8a8_gemm -- C = A W^T with both operands held one int8 code per
+ * element, per-group scales on both.
+ *
+ * Defines: "Experiment -- Hadamard rotation for int4 (W4A4) accuracy",
+ * Results (the W8A8 rows: int8 activations and weights); with codes in
+ * -8..7 it is the W4A4 GEMM of hr_w4a4_gemm with its codes held in int8, the
+ * form an int8 MAC consumes directly (no nibble unpacking in the kernel).
+ * The sums and the scale fusion are those of hr_w4a4_gemm.
+ *
+ *   acc[m][n][g] = sum_{k = gG}^{gG+G-1} A[m][k] W[n][k]      (exact int32)
+ *   C[m][n]      = sum_g sA[m][g] sW[n][g] acc[m][n][g]       (fp32)
+ *
+ *   a_codes   [M][K] int8 (activations, K contiguous).
+ *   w_codes   [N][K] int8 (weights, K contiguous).
+ *   Every int8 value is accepted.
+ *   other arguments, sizes and errors as hr_w4a4_gemm.
+ */
+int32_t hr_w8a8_gemm(const int8_t* a_codes, const void* a_scales,
+                     const int8_t* w_codes, const void* w_scales,
                      int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
                      int32_t group, float* c, int32_t* group_acc, void* stream);
 

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert hr.lib.hr_abi_version() == 2
+    assert hr.lib.hr_abi_version() == 3
     for st in (hr.HR_OK, hr.HR_EINVAL, hr.HR_EUNSUPPORTED, hr.HR_EDEVICE):
         assert hr.lib.hr_status_string(st).startswith(b"HR_")
     assert b"unknown" in hr.lib.hr_status_string(99)
@@ -132,7 +132,7 @@ def test_dequant_validation():
     assert f(P, P, hr.HR_F16, 0, 256, 128, P, None) == hr.HR_OK
 
 
-@pytest.mark.parametrize("fn", ["hr_w4a4_gemm", "hr_w4a8_gemm"])
+@pytest.mark.parametrize("fn", ["hr_w4a4_gemm", "hr_w4a8_gemm", "hr_w8a8_gemm"])
 def test_gemm_validation(fn):
     f = getattr(hr.lib, fn)
     # a, sa, w, sw, sdt, M, N, K, group, c, acc, stream
