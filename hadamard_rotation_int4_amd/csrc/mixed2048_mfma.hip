@@ -13,15 +13,15 @@
 // One workgroup of 8 waves per row, persistent over rows, two per CU.
 //   Phase 1: wave c < m transforms chunk c of the row with the matrix-core
 //     routine of mfma2048.h (its next row's chunk already in registers) and
-//     writes Z_c = H_2048 D_c x_c to LDS in natural element order: the
-//     16-byte slot j of 128-element block a sits at 32 a + (j ^ a), so the 16
-//     lanes of a write phase (16 different a) and of a read phase (16
-//     consecutive j) hit 16 different bank groups.
-//   Phase 2: every wave takes 256 positions of all m chunks (lane: 4
-//     consecutive positions), reads each Z_c once, mixes y_b = sum_c O[b][c]
-//     Z_c (m fmas per output; log2 m add/sub stages for O = H_m) and
-//     quantizes: the G / 4 lanes of a group reduce its absmax by DPP and
-//     permlane swaps, and each lane stores its 4 codes (16 bits) per chunk.
+//     writes Z_c = H_2048 D_c x_c to LDS, 128-element block a in 32 16-byte
+//     slots at 32 a + zslot(j, a) (conflict-free writes and reads).
+//   Phase 2: wave w takes 512 positions and half of the output chunks; a
+//     lane reads 8 of these positions (two 16-byte slots) of every Z_c and
+//     mixes them, y_b = sum_c O[b][c] Z_c, on the matrix cores as fp32 4x4x1
+//     products (the Sylvester block O = H_M by add/sub stages), then
+//     quantizes: the G / 8 lanes of a group reduce its absmax by DPP (and a
+//     permlane swap for G = 256), and each lane stores its 8 codes (32 bits)
+//     per output chunk.
 #include "mfma2048.h"
 
 namespace hr {
@@ -35,12 +35,12 @@ __device__ __forceinline__ uint32_t umax_row_pair(uint32_t a) {
   const uint32_t x = s[0], y = s[1];
   return x > y ? x : y;
 }
-// Max over lanes l and l ^ 32.
-__device__ __forceinline__ uint32_t umax_half_pair(uint32_t a) {
-  const auto s = __builtin_amdgcn_permlane32_swap(a, a, false, false);
-  const uint32_t x = s[0], y = s[1];
-  return x > y ? x : y;
-}
+// LDS slot of 16-byte slot j (0..31) of 128-element block a (0..15).  A
+// 16-byte access is served 8 lanes at a time, so every aligned group of 8
+// lanes must reach 8 different 16-byte bank groups (mod 8), and 16 lanes 16
+// (mod 16): phase-1 writes (one j, blocks a of a lane group) and phase-2 reads
+// (one block; slots 2k, 2k + 1, k or k + 16 for k = 0..15) both do.
+__device__ __forceinline__ int zslot(int j, int a) { return j ^ ((j >> 3) & 1) ^ ((j & 16) >> 1) ^ a; }
 
 template <int M, int G, bool SF16, bool OUT_F32, bool SYLV>
 __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfma_kernel(
@@ -74,14 +74,34 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
     for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const u32x4*>(base + 32 * s);
   };
 
-  // phase 2 placement: 128-position block gam, positions 128 gam + 4 k .. + 3
-  const int k = lane & 31;
-  const int gam = 2 * w + (lane >> 5);
-  const int rslot = 32 * gam + (k ^ gam);
-  const int pos = 128 * gam + 4 * k;
+  // phase 2 placement: wave w forms the output chunks ob .. ob + nout - 1
+  // (half w & 1 of the M outputs) at positions 512 (w >> 1) .. + 511; the 16
+  // lanes of DPP row gam = 4 (w >> 1) + lane / 16 cover block gam.  Lane
+  // k = lane & 15 takes two 16-byte slots of it: 2k and 2k + 1 (8 consecutive
+  // positions, one 32-bit code word) for quantization, k and k + 16 for the
+  // fp32 store (each store instruction then fills whole lines)
+  constexpr int OA = (M + 1) / 2;
+  const int ob = (w & 1) ? OA : 0;
+  const int nout = (w & 1) ? M - OA : OA;
+  const int k = lane & 15;
+  const int gam = 4 * (w >> 1) + (lane >> 4);
+  const int j0 = OUT_F32 ? k : 2 * k, j1 = OUT_F32 ? k + 16 : 2 * k + 1;
+  const int rs0 = 32 * gam + zslot(j0, gam), rs1 = 32 * gam + zslot(j1, gam);
+  const int pos = 128 * gam + 4 * j0;             // the second slot: pos + 4 (j1 - j0)
   // phase 1 leaves every value of block gam multiplied by the same sign
   // tau(gam); the mixing is linear, so it is folded into the output multiplier
   const float taug = (__builtin_popcount(gam) & 1) ? -1.0f : 1.0f;
+  // A operand of the 4x4x1 products (dense O): every 4-lane block holds rows
+  // ob .. ob + 3 of O (zero past the wave's outputs), the lane row ob + (lane & 3)
+  float coef[M];
+  if (!SYLV) {
+    const int ri = lane & 3, rw = ob + ri;
+#pragma unroll
+    for (int c = 0; c < M; ++c) {
+      const float o = block[ri < nout ? rw * M + c : 0];   // in bounds for every lane
+      coef[c] = ri < nout ? o : 0.0f;
+    }
+  }
 
   u32x4 nxt[4];
   if (xw && (int64_t)blockIdx.x < rows) load_chunk(blockIdx.x, nxt);
@@ -113,118 +133,138 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int j = (t & 1) + 2 * g + 8 * ((t >> 1) & 1) + 16 * (t >> 2);
-        zbuf[w][32 * a4 + (j ^ a4)] = acc[t];
+        zbuf[w][32 * a4 + zslot(j, a4)] = acc[t];
       }
     }
     __syncthreads();
 
-    // this lane's 4 positions of every chunk; with O = H_M they become the
-    // outputs in place (log2 M stages of (u + v, u - v) on chunk pairs)
-    f32x4 z[M];
+    // this lane's 8 positions of every chunk (two 16-byte slots)
+    f32x4 z[M][2];
 #pragma unroll
-    for (int c = 0; c < M; ++c) z[c] = zbuf[c][rslot];
-    __syncthreads();                              // zbuf is rewritten by the next row
-    if (SYLV) {
-#pragma unroll
-      for (int hb = 1; hb < M; hb <<= 1)
-#pragma unroll
-        for (int c = 0; c < M; ++c)
-          if (!(c & hb)) {
-            const f32x4 u = z[c], v = z[c | hb];
-            z[c] = u + v;
-            z[c | hb] = u - v;
-          }
+    for (int c = 0; c < M; ++c) {
+      z[c][0] = zbuf[c][rs0];
+      z[c][1] = zbuf[c][rs1];
     }
-    // output chunk bo: y = sum_c O[bo][c] Z_c (or the butterfly result)
-    auto out_chunk = [&](int bo) -> f32x4 {
-      if (SYLV) return z[bo];
-      f32x4 acc = z[0] * block[bo * M];
+    __syncthreads();                            // zbuf is rewritten by the next row
+    // acc[e][r] = y_{ob + r} at the lane's position e
+    f32x4 acc[8];
+    if constexpr (SYLV) {
+      // H_M = H_2 kron H_{M/2}: the wave's half (w & 1) of the outputs is
+      // H_{M/2} applied to u_c = Z_c +- Z_{c + M/2}; in-place add/sub stages
+      // leave output r in u[r]
+      constexpr int H2 = M / 2;
+      const float sg = (w & 1) ? -1.0f : 1.0f;
+      f32x4 u[H2][2];
 #pragma unroll
-      for (int c = 1; c < M; ++c) {
-        const float o = block[bo * M + c];
-        acc = (f32x4){fmaf(o, z[c][0], acc[0]), fmaf(o, z[c][1], acc[1]), fmaf(o, z[c][2], acc[2]),
-                      fmaf(o, z[c][3], acc[3])};
-      }
-      return acc;
-    };
-
-    if (OUT_F32) {
+      for (int c = 0; c < H2; ++c)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) u[c][s2][e] = fmaf(sg, z[c + H2][s2][e], z[c][s2][e]);
+#pragma unroll
+      for (int hb = 1; hb < H2; hb <<= 1)
+#pragma unroll
+        for (int c = 0; c < H2; ++c)
+          if (!(c & hb)) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const f32x4 a = u[c][s2], b = u[c | hb][s2];
+              u[c][s2] = a + b;
+              u[c | hb][s2] = a - b;
+            }
+          }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[e][r] = r < H2 ? u[r][e >> 2][e & 3] : 0.0f;
+    } else {
+      // y_{ob + r} = sum_c O[ob + r][c] Z_c at the lane's 8 positions: one
+      // 4x4x1 fp32 matrix-core product per position and c (A: the lane's
+      // coefficient, B: the lane's own Z value), rows r of acc[e] = outputs
+#pragma unroll
+      for (int c = 0; c < M; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_4x4x1f32(coef[c], z[c][e >> 2][e & 3],
+                                                       c == 0 ? (f32x4){0.0f, 0.0f, 0.0f, 0.0f} : acc[e],
+                                                       0, 0, 0);
+    }
+    if constexpr (OUT_F32) {
       const float ym = norm * taug;
 #pragma unroll
-      for (int bo = 0; bo < M; ++bo) {
-        const f32x4 v = out_chunk(bo);
-        __builtin_nontemporal_store((f32x4){v[0] * ym, v[1] * ym, v[2] * ym, v[3] * ym},
-                                    reinterpret_cast<f32x4*>(yout + row * NR + (int64_t)bo * P + pos));
+      for (int r = 0; r < OA; ++r) {
+        if (r >= nout) break;
+        float* dst = yout + row * NR + (int64_t)(ob + r) * P + pos;
+        __builtin_nontemporal_store((f32x4){acc[0][r] * ym, acc[1][r] * ym, acc[2][r] * ym, acc[3][r] * ym},
+                                    reinterpret_cast<f32x4*>(dst));
+        __builtin_nontemporal_store((f32x4){acc[4][r] * ym, acc[5][r] * ym, acc[6][r] * ym, acc[7][r] * ym},
+                                    reinterpret_cast<f32x4*>(dst + 64));
       }
-      continue;
-    }
-    // this row's codes and scales through buffer resources (32-bit offsets)
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        codes + row * (NR / 2), 0, (int)(NR / 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<char*>(scales) + row * (NR / G) * (SF16 ? 2 : 4), 0, (int)(NR / G) * (SF16 ? 2 : 4),
-        0x00020000);
-    // group absmax of the unnormalised outputs over the G / 4 lanes of a
-    // group; two chunks at a time, so that each DPP step reads a value
-    // written two instructions earlier (no wait states)
-    auto absmax4 = [](const f32x4& v) {
-      return __float_as_uint(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-    };
-    auto reduce2 = [](uint32_t& a0, uint32_t& a1) {
-      a0 = umax_dpp<kQuadXor1>(a0);
-      a1 = umax_dpp<kQuadXor1>(a1);
-      a0 = umax_dpp<kQuadXor2>(a0);
-      a1 = umax_dpp<kQuadXor2>(a1);
-      a0 = umax_dpp<kRowHalfMirror>(a0);          // 8 lanes: 32 positions
-      a1 = umax_dpp<kRowHalfMirror>(a1);
+    } else {
+      // this row's codes and scales through buffer resources (32-bit offsets)
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+          codes + row * (NR / 2), 0, (int)(NR / 2), 0x00020000);
+      const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<char*>(scales) + row * (NR / G) * (SF16 ? 2 : 4), 0, (int)(NR / G) * (SF16 ? 2 : 4),
+          0x00020000);
+      // group absmax of the unnormalised outputs over the G / 8 lanes of a
+      // group, all output rows interleaved (each DPP step reads a value
+      // written several instructions earlier: no wait states)
+      uint32_t am[OA];
+#pragma unroll
+      for (int r = 0; r < OA; ++r) {
+        float m = fmaxf(fmaxf(fabsf(acc[0][r]), fabsf(acc[1][r])), fabsf(acc[2][r]));
+        m = fmaxf(fmaxf(m, fabsf(acc[3][r])), fabsf(acc[4][r]));
+        m = fmaxf(fmaxf(m, fabsf(acc[5][r])), fabsf(acc[6][r]));
+        am[r] = __float_as_uint(fmaxf(m, fabsf(acc[7][r])));
+      }
+#pragma unroll
+      for (int r = 0; r < OA; ++r) am[r] = umax_dpp<kQuadXor1>(am[r]);
+#pragma unroll
+      for (int r = 0; r < OA; ++r) am[r] = umax_dpp<kQuadXor2>(am[r]);
       if (G >= 64) {
-        a0 = umax_dpp<kRowMirror>(a0);
-        a1 = umax_dpp<kRowMirror>(a1);
+#pragma unroll
+        for (int r = 0; r < OA; ++r) am[r] = umax_dpp<kRowHalfMirror>(am[r]);   // 8 lanes: 64 positions
       }
       if (G >= 128) {
-        a0 = umax_row_pair(a0);
-        a1 = umax_row_pair(a1);
+#pragma unroll
+        for (int r = 0; r < OA; ++r) am[r] = umax_dpp<kRowMirror>(am[r]);
       }
       if (G >= 256) {
-        a0 = umax_half_pair(a0);
-        a1 = umax_half_pair(a1);
-      }
-    };
-    // scale, codes and stores of chunk bo from its group absmax ab
-    auto quant_chunk = [&](int bo, const f32x4& v, uint32_t ab) {
-      const float s32 = div_const<7>(__uint_as_float(ab) * norm);
-      const float sq = SF16 ? (float)(_Float16)s32 : s32;
-      const float kq = sq > 0.0f ? norm * taug * __builtin_amdgcn_rcpf(sq) : 0.0f;
-      // the first lane of each group stores its scale
-      if ((lane & (G / 4 - 1)) == 0) {
-        const int so = (bo * (P / G) + pos / G) * (SF16 ? 2 : 4);
-        if (SF16)
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)s32), rsc, so, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32), rsc, so, 0, 0);
-      }
-      // q + 1.5 * 2^23 + 8 rounds y k to an integer in the low mantissa bits
-      // (ties to even); its low byte is q + 8 in [1, 15].  The clamp to
-      // [-7, 7] only acts for fp16-subnormal (or fp32-denormal) scales, whose
-      // reciprocal is imprecise; elsewhere |y k| rounds to at most 7.
-      constexpr float MQ = 12582920.0f;
-      float r[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r[e] = __builtin_amdgcn_fmed3f(fmaf(v[e], kq, MQ), MQ - 7.0f, MQ + 7.0f);
-      const uint32_t p01 = (__float_as_uint(r[1]) << 4) | __float_as_uint(r[0]);
-      const uint32_t p23 = (__float_as_uint(r[3]) << 4) | __float_as_uint(r[2]);
-      const uint32_t c16 = (((p23 << 8) | (p01 & 0xFFu)) & 0xFFFFu) ^ 0x8888u;
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)c16, rc, pos / 2, bo * (P / 2), 0);
-    };
+        for (int r = 0; r < OA; ++r) am[r] = umax_row_pair(am[r]);
+      }
 #pragma unroll
-    for (int bo = 0; bo < M; bo += 2) {
-      const f32x4 v0 = out_chunk(bo);
-      const f32x4 v1 = out_chunk(bo + 1 < M ? bo + 1 : bo);
-      uint32_t a0 = absmax4(v0), a1 = absmax4(v1);
-      reduce2(a0, a1);
-      quant_chunk(bo, v0, a0);
-      if (bo + 1 < M) quant_chunk(bo + 1, v1, a1);
+      for (int r = 0; r < OA; ++r) {
+        if (r >= nout) break;
+        const int bo = ob + r;
+        const float s32 = div_const<7>(__uint_as_float(am[r]) * norm);
+        const float sq = SF16 ? (float)(_Float16)s32 : s32;
+        const float kq = sq > 0.0f ? norm * taug * __builtin_amdgcn_rcpf(sq) : 0.0f;
+        // the first lane of each group stores its scale
+        if ((lane & (G / 8 - 1)) == 0) {
+          const int so = (bo * (P / G) + pos / G) * (SF16 ? 2 : 4);
+          if (SF16)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)s32), rsc, so, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32), rsc, so, 0, 0);
+        }
+        // q + 1.5 * 2^23 + 8 rounds y k to an integer in the low mantissa
+        // bits (ties to even); its low byte is q + 8 in [1, 15].  The clamp
+        // to [-7, 7] only acts for fp16-subnormal (or fp32-denormal) scales,
+        // whose reciprocal is imprecise; elsewhere |y k| rounds to at most 7.
+        constexpr float MQ = 12582920.0f;
+        uint32_t q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          q[e] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(acc[e][r], kq, MQ), MQ - 7.0f, MQ + 7.0f));
+        // nibble e of the word is code e; low bytes of the pairs first
+        const uint32_t p01 = (q[1] << 4) | q[0], p23 = (q[3] << 4) | q[2];
+        const uint32_t p45 = (q[5] << 4) | q[4], p67 = (q[7] << 4) | q[6];
+        const uint32_t word =
+            ((p01 & 0xFFu) | ((p23 & 0xFFu) << 8) | ((p45 & 0xFFu) << 16) | (p67 << 24)) ^ 0x88888888u;
+        __builtin_amdgcn_raw_buffer_store_b32(word, rc, pos / 2, bo * (P / 2), 0);
+      }
     }
   }
 }
