@@ -54,6 +54,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   HR_F4(120, 121, 122, 123, b, CTRL) \
   HR_F4(124, 125, 126, 127, b, CTRL)
 
+// Max over lanes l and l ^ 16 (permlane16_swap exchanges odd and even rows).
+__device__ __forceinline__ uint32_t umax_row_pair(uint32_t a) {
+  const auto s = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  const uint32_t x = s[0], y = s[1];
+  return x > y ? x : y;
+}
+
 // Max over the four lanes q, q + 16, q + 32, q + 48 (same DPP-row position).
 __device__ __forceinline__ float max_over_rows(float m) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);

@@ -29,12 +29,6 @@ namespace hr {
 constexpr int kMixWaves = 8;
 constexpr int kMixBlocksPerCu = 2;
 
-// Max over lanes l and l ^ 16 (permlane16_swap exchanges odd and even rows).
-__device__ __forceinline__ uint32_t umax_row_pair(uint32_t a) {
-  const auto s = __builtin_amdgcn_permlane16_swap(a, a, false, false);
-  const uint32_t x = s[0], y = s[1];
-  return x > y ? x : y;
-}
 // LDS slot of 16-byte slot j (0..31) of 128-element block a (0..15).  A
 // 16-byte access is served 8 lanes at a time, so every aligned group of 8
 // lanes must reach 8 different 16-byte bank groups (mod 8), and 16 lanes 16
