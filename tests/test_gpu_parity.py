@@ -217,6 +217,42 @@ def test_mixed_radix_many_rows(m, group, with_signs, scale_mode):
     check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, scale_mode)
 
 
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 6, 7, 8])
+def test_mixed_radix_grid(m, group):
+    """Every block size of the bf16 matrix-core kernel against every group
+    size: the waves split the m output chunks into halves of (m + 1) // 2 and
+    m // 2, and the group absmax takes 2 to 5 lane-reduction steps."""
+    hr = _hr()
+    rows, p = 5, 2048
+    mi = hr_inputs.mixed_inputs(rows=rows, m=m, p=p, seed=700 + 10 * m + group)
+    xd = mi.x.to(DEV)
+    dd = torch.from_numpy(mi.signs).to(DEV)
+    od = torch.from_numpy(mi.block).to(DEV)
+    y64 = oracle.mixed_radix.mixed_radix(mi.x.float().numpy(), mi.signs, mi.block, p)
+    codes, scales = hr.rotate_quant_int4(xd, group, dd, od)
+    check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, "f16")
+    if group == 128:
+        check_rotated(hr.rotate(xd, dd, od).cpu().numpy(), y64)
+
+
+@pytest.mark.parametrize("group", [32, 64, 128, 256])
+@pytest.mark.parametrize("n", [4096, 8192, 16384])
+def test_sylvester_chunks_grid(n, group):
+    """n = 4096 (few rows), 8192 and 16384 as H_{n/2048} kron H_2048 in the
+    mixed-radix kernel (each wave's half of the outputs by one +- stage, then
+    add/sub stages), every group size."""
+    hr = _hr()
+    rows = 7
+    x, d = _bf16_rows(rows, n, seed=900 + n // 1024 + group)
+    dd = torch.from_numpy(d).to(DEV)
+    y64 = oracle.hadamard.rht(x.float().numpy(), d)
+    codes, scales = hr.rotate_quant_int4(x.to(DEV), group, dd)
+    check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, "f16")
+    if group == 128:
+        check_rotated(hr.rotate(x.to(DEV), dd).cpu().numpy(), y64)
+
+
 def test_mixed_radix_fp32_input_fp32_scales():
     hr = _hr()
     m, p, group = 5, 2048, 128
