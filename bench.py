@@ -150,6 +150,9 @@ def main(argv=None):
     ap.add_argument("--only-main", action="store_true", help="time only the headline kernel")
     ap.add_argument("--profile-gemm", action="store_true",
                     help="run only the 4096^3 W4A4 and W4A8 GEMMs, --steps times each (for counters)")
+    ap.add_argument("--profile-mixed", action="store_true",
+                    help="run only the bf16 16384x14336 (m = 7) mixed-radix quantization, --steps times "
+                         "(for counters)")
     ap.add_argument("--profile-run", action="store_true",
                     help="run the headline kernel and a plain copy (for rocprofv3 --pmc), print nothing")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -191,6 +194,17 @@ def main(argv=None):
                                         (hr.w4a8_gemm, t(g8.a_codes), t(g8.a_scales))):
             for _ in range(args.steps):
                 call(a_codes, a_scales, wd, swd, 128, out=cg)
+        torch.cuda.synchronize()
+        return 0
+
+    if args.profile_mixed:
+        mi = hr_inputs.mixed_inputs()
+        xm = mi.x.to(dev)
+        dm, om = torch.from_numpy(mi.signs).to(dev), torch.from_numpy(mi.block).to(dev)
+        cm = torch.empty((mi.rows, mi.m * mi.p // 2), dtype=torch.uint8, device=dev)
+        sm = torch.empty((mi.rows, mi.m * mi.p // 128), dtype=torch.float16, device=dev)
+        for _ in range(args.steps):
+            hr.rotate_quant_int4(xm, 128, dm, om, codes=cm, scales=sm)
         torch.cuda.synchronize()
         return 0
 
@@ -427,21 +441,20 @@ GEMM_COUNTER_PASSES = (
 )
 
 
-def _summarize_gemm_counters(d):
-    """Per-dispatch counter averages of the two 4096^3 tile kernels, from the
-    passes under d/gemm_p1, d/gemm_p2 (one rocprofv3 --pmc run each)."""
+def _summarize_counters(d, prefix, kernels, out_name, title, run_flag):
+    """Per-dispatch counter averages of the named kernels from the passes under
+    d/<prefix>1, d/<prefix>2 (one rocprofv3 --pmc run each)."""
     rows = []
     for i in range(1, len(GEMM_COUNTER_PASSES) + 1):
-        rows += _read_csv(os.path.join(d, f"gemm_p{i}", "**", "*counter_collection.csv"))
+        rows += _read_csv(os.path.join(d, f"{prefix}{i}", "**", "*counter_collection.csv"))
     if not rows:
         return
-    lines = ["# rocprofv3 --pmc counters, per dispatch, of the 4096^3 G=128 fp16-scale GEMM tile kernels",
-             "# command, one per pass: rocprofv3 --pmc <pass> -d <dir>/gemm_p<i> -o run --output-format csv "
-             "-- python bench.py --profile-gemm --steps 10"]
+    lines = [f"# rocprofv3 --pmc counters, per dispatch, of {title}",
+             f"# command, one per pass: rocprofv3 --pmc <pass> -d <dir>/{prefix}<i> -o run --output-format csv "
+             f"-- python bench.py {run_flag} --steps 10"]
     for i, pmc in enumerate(GEMM_COUNTER_PASSES, 1):
         lines.append(f"# pass {i}: {pmc}")
-    for label, name in (("W4A4", "w4a4_gemm_tile_kernel<128, true, false, false>"),
-                        ("W4A8", "w4a4_gemm_tile_kernel<128, true, false, true>")):
+    for label, name in kernels:
         vals = {}
         for pmc in " ".join(GEMM_COUNTER_PASSES).split():
             v, n = _counter_per_dispatch(rows, name, pmc)
@@ -461,8 +474,25 @@ def _summarize_gemm_counters(d):
         mb, co = vals.get("SQ_VALU_MFMA_BUSY_CYCLES"), vals.get("SQ_VALU_MFMA_COEXEC_CYCLES")
         if mb and co is not None:
             lines.append(f"  VALU co-issued during MFMA-busy cycles = {co / mb:.4f}")
-    with open(os.path.join(PROFILES, "w4a4_w4a8_gemm_4096_g128.counters.txt"), "w") as f:
+        wv = vals.get("SQ_WAVES")
+        if wv and va:
+            lines.append(f"  VALU instructions per wave = {va / wv:.1f}")
+    with open(os.path.join(PROFILES, out_name), "w") as f:
         f.write("\n".join(lines) + "\n")
+
+
+def _summarize_gemm_counters(d):
+    _summarize_counters(d, "gemm_p", (("W4A4", "w4a4_gemm_tile_kernel<128, true, false, false>"),
+                                      ("W4A8", "w4a4_gemm_tile_kernel<128, true, false, true>")),
+                        "w4a4_w4a8_gemm_4096_g128.counters.txt",
+                        "the 4096^3 G=128 fp16-scale GEMM tile kernels", "--profile-gemm")
+
+
+def _summarize_mixed_counters(d):
+    _summarize_counters(d, "mixed_p", (("mixed radix m = 7", "mixed2048_mfma_kernel<7, 128, true, false, false>"),),
+                        "mixed_radix_quant_bf16_16384x14336_g128.counters.txt",
+                        "the bf16 16384x14336 (m = 7, O_7 dense) G=128 mixed-radix quantization kernel",
+                        "--profile-mixed")
 
 
 def summarize_profile(d):
@@ -501,6 +531,7 @@ def summarize_profile(d):
            "copy_kernel_match": copy_kernel, "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf,
            "copy_write_kib": cw, "copy_dispatches": nc}
     _summarize_gemm_counters(d)
+    _summarize_mixed_counters(d)
     if None not in (kf, kw, cf, cw):
         ff = COPY_BYTES / (cf * 1024.0)
         fw = COPY_BYTES / (cw * 1024.0)
