@@ -107,3 +107,63 @@ def test_quant_dequant_error_bound():
 def test_rejects_group_not_dividing():
     with pytest.raises(ValueError):
         Q.quantize_groups(np.zeros((1, 10)), 4)
+
+
+# ---- t_values: the value whose rounding decides each code.  The GPU parity
+# check excuses a code mismatch only where this value sits within 1e-4 of a
+# rounding midpoint, so it is pinned on its own.
+
+def test_t_values_exact_hand_built():
+    """Scales that are powers of two make y / s exact: the pin is the value
+    itself.  Group 0 has s = 1 (t = y), group 1 has s = 0.5 (t = 2 y), group 2
+    has s = 0 (treated as division by one; its codes are zero anyway)."""
+    y = np.array([[7.0, 2.5, -2.5, 0.5, -6.25, 1.5, -1.49, 0.0,
+                   3.5, 1.25, -0.75, 0.0, 0.5, -3.5, 2.0, 1.0,
+                   0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0]])
+    s = np.array([[1.0, 0.5, 0.0]], dtype=np.float32)
+    t = Q.t_values(y, s, 8)
+    assert t.dtype == np.float32
+    want = np.concatenate([y[0, :8], 2.0 * y[0, 8:16], y[0, 16:]]).astype(np.float32)
+    assert np.array_equal(t[0], want)
+
+
+def test_t_values_uses_the_given_scale_not_the_absmax():
+    """With an fp16 scale the quotient is taken against the stored scale: for
+    absmax 1, s = fp16(1/7) = 0.142822265625 (exactly 585 * 2^-12), so
+    t = fl32(y * 4096 / 585), and the absmax element lands above 7 (7.0017)
+    before the clamp."""
+    y = np.array([[1.0, 0.5, -0.25, 0.0]])
+    _, scales, s_used = Q.quantize_groups(y, 4, "f16")
+    assert float(s_used[0, 0]) == 585 * 2.0 ** -12
+    t = Q.t_values(y, s_used, 4)
+    assert t[0].tolist() == [np.float32(4096.0 / 585.0), np.float32(2048.0 / 585.0),
+                             np.float32(-1024.0 / 585.0), 0.0]
+    assert t[0, 0] > 7.0
+
+
+def test_t_values_decide_the_codes_away_from_midpoints():
+    """On random data, round-half-away of t, clamped, equals the oracle's codes
+    wherever t is at least 1e-4 from a rounding midpoint, in both scale modes and
+    at both bit widths; the window excludes only a small fraction of elements."""
+    rng = np.random.default_rng(11)
+    y = rng.standard_normal((32, 1024)) * rng.uniform(1e-3, 1e3, size=(32, 1))
+    for bits in (4, 8):
+        qmax = (1 << (bits - 1)) - 1
+        for mode in ("f16", "f32"):
+            codes, _, s_used = Q.quantize_groups(y, 64, mode, bits)
+            t = Q.t_values(y, s_used, 64).astype(np.float64)
+            frac = np.abs(t) - np.floor(np.abs(t))
+            away = np.abs(frac - 0.5) >= 1e-4
+            q = np.clip(np.sign(t) * np.floor(np.abs(t) + 0.5), -qmax, qmax)
+            assert np.array_equal(q[away], codes[away].astype(np.float64))
+            assert away.mean() > 0.999
+
+
+def test_t_values_midpoints_are_found():
+    """Exact midpoints k + 1/2 (scale 1) are inside the window, values 2e-4 away
+    from one are outside it."""
+    y = np.array([[7.0, 2.5, -3.5, 2.5002, 1.4998, 0.0, 4.0, -6.5]])
+    t = Q.t_values(y, np.array([[1.0]], dtype=np.float32), 8).astype(np.float64)
+    frac = np.abs(t) - np.floor(np.abs(t))
+    near = np.abs(frac - 0.5) < 1e-4
+    assert near[0].tolist() == [False, True, True, False, False, False, False, True]
