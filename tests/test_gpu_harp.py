@@ -44,6 +44,17 @@ SCHEDULES = [(8, 8, 8, 5, 2), (4, 5, 3, 2), (2,) * 6, (7, 4, 2), (6, 4), (3, 3, 
              (2, 2)]
 
 
+def _oracle_blocks(hi):
+    """The oracle's own blocks from theta (fp64 throughout)."""
+    return H.blocks(hi.radices, hi.theta, hi.fallbacks)
+
+
+def _oracle_blocks_stored(hi):
+    """The oracle's blocks rounded once to fp32: what hr_harp_blocks documents
+    it stores (each block formed in double precision, stored as fp32)."""
+    return [b.astype(np.float32).astype(np.float64) for b in _oracle_blocks(hi)]
+
+
 @pytest.mark.parametrize("radices", SCHEDULES)
 def test_harp_blocks(radices):
     hi = hr_inputs.harp_inputs(rows=1, radices=radices, seed=60 + len(radices))
@@ -135,3 +146,66 @@ def test_harp_4096x5120_sampled():
     none, codes2, scales2 = hr.harp_apply(_t(hi.x), hi.radices, blk, want_y=False, group=128)
     assert none is None
     assert torch.equal(codes2, codes) and torch.equal(scales2, scales)
+
+
+# ---- end to end from theta: the GPU's block table and application against
+# the oracle's own blocks (no GPU data enters the reference)
+
+@pytest.mark.parametrize("radices,rows", [((8, 8, 8, 5, 2), 131), ((4, 5, 3, 2), 97), ((2,) * 6, 64),
+                                          ((7, 4, 2), 33), ((6, 4), 40), ((3, 3, 4), 50),
+                                          ((8, 8, 8, 8), 21), ((2, 2), 9)])
+def test_harp_theta_to_output(radices, rows):
+    """Forward and inverse output from theta, against the oracle's fp64 blocks
+    at 2e-5 x row max; the oracle's fp32-stored blocks at the same bound."""
+    hr = _hr()
+    hi = hr_inputs.harp_inputs(rows=rows, radices=radices, seed=90 + rows)
+    blk = _gpu_blocks(hi)
+    y = hr.harp_apply(_t(hi.x), hi.radices, blk).cpu().numpy()
+    yi = hr.harp_apply(_t(hi.x), hi.radices, blk, inverse=True).cpu().numpy()
+    for ob in (_oracle_blocks(hi), _oracle_blocks_stored(hi)):
+        check_rotated(y, H.apply(hi.x, hi.radices, ob))
+        check_rotated(yi, H.apply(hi.x, hi.radices, ob, inverse=True))
+
+
+@pytest.mark.parametrize("radices,group,scale_mode", [((8, 8, 8, 5, 2), 128, "f16"),
+                                                      ((8, 8, 8, 5, 2), 32, "f32"),
+                                                      ((5, 8, 8), 64, "f16"),
+                                                      ((3, 8, 8, 2), 128, "f32"),
+                                                      ((8, 8, 8, 8), 256, "f16"),
+                                                      ((2,) * 6, 64, "f32")])
+def test_harp_theta_to_codes(radices, group, scale_mode):
+    """Quantized output from theta: rotated values against the oracle's fp64
+    blocks; codes and scales against the oracle's quantization of its own
+    application of the stored (fp32-rounded) blocks."""
+    hr = _hr()
+    hi = hr_inputs.harp_inputs(rows=77, radices=radices, seed=95 + group)
+    blk = _gpu_blocks(hi)
+    sd = torch.float16 if scale_mode == "f16" else torch.float32
+    y, codes, scales = hr.harp_apply(_t(hi.x), hi.radices, blk, group=group, scale_dtype=sd)
+    check_rotated(y.cpu().numpy(), H.apply(hi.x, hi.radices, _oracle_blocks(hi)))
+    y64 = H.apply(hi.x, hi.radices, _oracle_blocks_stored(hi))
+    check_rotated(y.cpu().numpy(), y64)
+    check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, scale_mode)
+
+
+def test_harp_two_sided():
+    """HARP's two-sided use (abstract: a two-sided orthogonal processor with
+    exact full-precision equivalence): with x' = Q_i x, W' = Q_o W Q_i^T, the
+    product W' x' equals Q_o (W x).  Q_i (d_in = 5120, (8, 8, 8, 5, 2)) is
+    applied on the GPU to the rows of X and of W, Q_o (d_out = 1152,
+    (8, 8, 3, 6)) to the columns of W Q_i^T; the product of the transformed
+    operands is checked against the oracle's Q_o applied to X W^T."""
+    hr = _hr()
+    hi = hr_inputs.harp_inputs(rows=48, radices=(8, 8, 8, 5, 2), seed=97)
+    ho = hr_inputs.harp_inputs(rows=1, radices=(8, 8, 3, 6), seed=98)
+    W = np.random.default_rng(99).standard_normal((ho.d, hi.d)).astype(np.float32)
+    bi, bo = _gpu_blocks(hi), _gpu_blocks(ho)
+    xp = hr.harp_apply(_t(hi.x), hi.radices, bi)                       # rows x -> Q_i x
+    wqi = hr.harp_apply(_t(W), hi.radices, bi)                          # rows of W Q_i^T
+    wp = hr.harp_apply(wqi.t().contiguous(), ho.radices, bo).t()        # Q_o on its columns
+    yp = xp.cpu().numpy().astype(np.float64) @ wp.cpu().numpy().astype(np.float64).T
+    y_ref = H.apply(hi.x.astype(np.float64) @ W.astype(np.float64).T, ho.radices, _oracle_blocks(ho))
+    check_rotated(yp, y_ref)
+    # and undoing Q_o on the GPU gives back the original product W x
+    back = hr.harp_apply(_t(yp.astype(np.float32)), ho.radices, bo, inverse=True).cpu().numpy()
+    check_rotated(back, hi.x.astype(np.float64) @ W.astype(np.float64).T)
