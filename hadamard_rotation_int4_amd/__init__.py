@@ -1,12 +1,15 @@
 """Python binding of libhr.so (ctypes): randomized Hadamard rotation, fused
-int4 / int8 quantization, HARP-style butterfly, int4 dequant and the W4A4 /
-W4A8 GEMMs on MI355X (gfx950).
+int4 / int8 quantization, HARP-style butterfly and mixed-radix processor, int4
+dequant, the W4A4 / W4A8 / W8A8 GEMMs and the online-rotation decode GEMM on
+MI355X (gfx950).
 
 Argument marshalling only: every step runs in the library's HIP kernels on
-torch's current stream.  Tensors must be CUDA tensors, contiguous, of the
-dtypes stated per function; outputs are allocated with torch when not given.
-The library must be built in-tree first (``python
-hadamard_rotation_int4_amd/build.py``); importing without it raises ImportError.
+torch's current stream.  Every tensor argument is checked (dtype, shape,
+contiguity, then device) against the sizes passed to the C call before the
+call is made, and outputs are allocated with torch when not given.  The
+library must be built in-tree first (``python
+hadamard_rotation_int4_amd/build.py``); importing without it, or with a
+library built from other sources, raises ImportError.
 """
 from __future__ import annotations
 
@@ -15,8 +18,11 @@ import os
 
 import torch
 
-__all__ = ["HRError", "rotate", "rotate_quant_int4", "rotate_quant_int8", "butterfly_coeffs",
-           "butterfly_apply", "harp_blocks", "harp_apply", "dequant_int4", "w4a4_gemm", "w4a8_gemm",
+from . import srchash
+
+__all__ = ["HRError", "rotate", "rotate_quant_int4", "rotate_quant_int8", "quant_int4", "quant_int8",
+           "butterfly_coeffs", "butterfly_apply", "harp_blocks", "harp_apply", "harp_n_params",
+           "dequant_int4", "w4a4_gemm", "w4a8_gemm", "w8a8_gemm", "rotate_quant_w4a4_gemm",
            "lib", "LIB_PATH", "SYMBOLS",
            "HR_OK", "HR_EINVAL", "HR_EUNSUPPORTED", "HR_EDEVICE", "HR_F32", "HR_BF16", "HR_F16"]
 
@@ -30,11 +36,14 @@ _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 # name -> (restype, argtypes); mirrors include/hr.h
 SYMBOLS = {
     "hr_abi_version": (_i32, []),
+    "hr_build_id": (ctypes.c_char_p, []),
     "hr_status_string": (ctypes.c_char_p, [_i32]),
     "hr_last_error": (ctypes.c_char_p, []),
     "hr_rotate": (_i32, [_vp, _i32, _vp, _i64, _i32, _i32, _vp, _vp, _vp]),
     "hr_rotate_quant_int4": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
     "hr_rotate_quant_int8": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp]),
+    "hr_quant_int4": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp]),
+    "hr_quant_int8": (_i32, [_vp, _i32, _i64, _i32, _i32, _vp, _vp, _i32, _vp]),
     "hr_butterfly_coeffs": (_i32, [_vp, _i32, _i32, _vp, _vp]),
     "hr_butterfly_apply": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _i32, _vp]),
     "hr_harp_blocks": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp]),
@@ -43,6 +52,8 @@ SYMBOLS = {
     "hr_w4a4_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "hr_w4a8_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "hr_w8a8_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "hr_rotate_quant_w4a4_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _vp,
+                                         _vp, _vp, _vp]),
 }
 
 
@@ -55,6 +66,11 @@ def _load() -> ctypes.CDLL:
         fn = getattr(handle, name)
         fn.restype = res
         fn.argtypes = args
+    built = handle.hr_build_id().decode()
+    want = srchash.source_hash()
+    if built != want:
+        raise ImportError(f"{LIB_PATH} was built from other sources (build id {built}, sources "
+                          f"{want}): rebuild it with `python hadamard_rotation_int4_amd/build.py`")
     return handle
 
 
@@ -73,16 +89,58 @@ def _check(status: int, fn: str) -> None:
         raise HRError(status, fn)
 
 
-def _ptr(t):
+_DT_NAME = {torch.float32: "float32", torch.bfloat16: "bfloat16", torch.float16: "float16",
+            torch.int8: "int8", torch.uint8: "uint8", torch.int32: "int32"}
+
+
+def _arg(t, name: str, dtypes, shape):
+    """Check tensor ``t``: dtype in ``dtypes``, exact ``shape``, contiguous.
+    Returns (name, t); None passes through.  Devices are checked afterwards
+    by _ptrs, so every dtype and shape error is reported first."""
     if t is None:
-        return None
+        return (name, None)
     if not isinstance(t, torch.Tensor):
-        raise TypeError("expected a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError("tensor must live on the GPU")
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if not isinstance(dtypes, (tuple, list)):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in "
+                        f"{[_DT_NAME.get(d, str(d)) for d in dtypes]}")
+    shape = tuple(int(v) for v in shape)
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {shape}")
     if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
-    return t.data_ptr()
+        raise ValueError(f"{name}: tensor must be contiguous")
+    return (name, t)
+
+
+def _ptrs(*args):
+    """Device pointers of checked tensors (None -> NULL): each must be a GPU
+    tensor, all on the device of the first one."""
+    dev = None
+    out = []
+    for name, t in args:
+        if t is None:
+            out.append(None)
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name}: tensor must live on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, expected {dev}")
+        out.append(t.data_ptr())
+    return out
+
+
+def _rows_of(x, name: str, dtypes):
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(x).__name__}")
+    if x.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D [rows][n] tensor, got shape {tuple(x.shape)}")
+    if x.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {x.dtype} not in {[_DT_NAME[d] for d in dtypes]}")
+    return int(x.shape[0]), int(x.shape[1])
 
 
 def _stream(device) -> int:
@@ -99,16 +157,68 @@ def _dtype_code(dt) -> int:
     raise TypeError(f"unsupported dtype {dt}")
 
 
+def _scale_dtype(dt):
+    if dt not in (torch.float16, torch.float32):
+        raise TypeError(f"scale_dtype must be torch.float16 or torch.float32, got {dt}")
+    return dt
+
+
+def _group(group, n: int) -> int:
+    g = int(group)
+    if g <= 0 or n % g:
+        raise ValueError(f"group={g} must be a positive divisor of the row length {n}")
+    return g
+
+
+def _block_m(block, n: int) -> int:
+    if block is None:
+        return 1
+    if not isinstance(block, torch.Tensor) or block.dim() != 2 or block.shape[0] != block.shape[1]:
+        raise ValueError("block must be a square [m][m] tensor")
+    m = int(block.shape[0])
+    if m < 1 or n % m:
+        raise ValueError(f"block size m={m} must divide the row length {n}")
+    return m
+
+
+# ------------------------------------------------------------------ rotation
+
 def rotate(x: torch.Tensor, signs: torch.Tensor | None = None, block: torch.Tensor | None = None,
            out: torch.Tensor | None = None) -> torch.Tensor:
     """y = (O kron H_p)(d * x)/sqrt(p) per row (hr_rotate).  x: [rows][n] bf16/fp32;
     signs: int8 [n] or None; block: fp32 [m][m] or None (m = 1)."""
-    rows, n = x.shape
-    m = 1 if block is None else int(block.shape[0])
+    rows, n = _rows_of(x, "x", (torch.bfloat16, torch.float32))
+    m = _block_m(block, n)
+    ax = _arg(x, "x", (torch.bfloat16, torch.float32), (rows, n))
+    asg = _arg(signs, "signs", torch.int8, (n,))
+    ab = _arg(block, "block", torch.float32, (m, m))
+    _arg(out, "out", torch.float32, (rows, n))
     y = out if out is not None else torch.empty((rows, n), dtype=torch.float32, device=x.device)
-    _check(lib.hr_rotate(_ptr(x), _dtype_code(x.dtype), _ptr(y), rows, n, m, _ptr(signs),
-                         _ptr(block), _stream(x.device)), "hr_rotate")
+    px, ps, pb, py = _ptrs(ax, asg, ab, ("out", y))
+    _check(lib.hr_rotate(px, _dtype_code(x.dtype), py, rows, n, m, ps, pb, _stream(x.device)), "hr_rotate")
     return y
+
+
+def _rotate_quant(fn, bits, x, group, signs, block, scale_dtype, codes, scales):
+    rows, n = _rows_of(x, "x", (torch.bfloat16, torch.float32))
+    m = _block_m(block, n)
+    g = _group(group, n)
+    sd = _scale_dtype(scales.dtype if isinstance(scales, torch.Tensor) else scale_dtype)
+    cdt, cshape = (torch.uint8, (rows, n // 2)) if bits == 4 else (torch.int8, (rows, n))
+    ax = _arg(x, "x", (torch.bfloat16, torch.float32), (rows, n))
+    asg = _arg(signs, "signs", torch.int8, (n,))
+    ab = _arg(block, "block", torch.float32, (m, m))
+    _arg(codes, "codes", cdt, cshape)
+    _arg(scales, "scales", sd, (rows, n // g))
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(cshape, dtype=cdt, device=dev)
+    if scales is None:
+        scales = torch.empty((rows, n // g), dtype=sd, device=dev)
+    px, ps, pb, pc, pq = _ptrs(ax, asg, ab, ("codes", codes), ("scales", scales))
+    _check(getattr(lib, fn)(px, _dtype_code(x.dtype), rows, n, m, ps, pb, g, pc, pq, _dtype_code(sd),
+                            _stream(dev)), fn)
+    return codes, scales
 
 
 def rotate_quant_int4(x: torch.Tensor, group: int, signs: torch.Tensor | None = None,
@@ -116,17 +226,7 @@ def rotate_quant_int4(x: torch.Tensor, group: int, signs: torch.Tensor | None = 
                       codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     """Fused rotation + per-group int4 quantization (hr_rotate_quant_int4).
     Returns (codes uint8 [rows][n/2], scales [rows][n/group] of scale_dtype)."""
-    rows, n = x.shape
-    m = 1 if block is None else int(block.shape[0])
-    if codes is None:
-        codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
-    if scales is None:
-        scales = torch.empty((rows, n // group), dtype=scale_dtype, device=x.device)
-    _check(lib.hr_rotate_quant_int4(_ptr(x), _dtype_code(x.dtype), rows, n, m, _ptr(signs),
-                                    _ptr(block), group, _ptr(codes), _ptr(scales),
-                                    _dtype_code(scales.dtype), _stream(x.device)),
-           "hr_rotate_quant_int4")
-    return codes, scales
+    return _rotate_quant("hr_rotate_quant_int4", 4, x, group, signs, block, scale_dtype, codes, scales)
 
 
 def rotate_quant_int8(x: torch.Tensor, group: int, signs: torch.Tensor | None = None,
@@ -134,25 +234,63 @@ def rotate_quant_int8(x: torch.Tensor, group: int, signs: torch.Tensor | None = 
                       codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
     """Fused rotation + per-group int8 quantization (hr_rotate_quant_int8).
     Returns (codes int8 [rows][n], scales [rows][n/group] of scale_dtype)."""
-    rows, n = x.shape
-    m = 1 if block is None else int(block.shape[0])
+    return _rotate_quant("hr_rotate_quant_int8", 8, x, group, signs, block, scale_dtype, codes, scales)
+
+
+def _quant(fn, bits, x, group, scale_dtype, codes, scales):
+    rows, n = _rows_of(x, "x", (torch.bfloat16, torch.float32))
+    g = _group(group, n)
+    sd = _scale_dtype(scales.dtype if isinstance(scales, torch.Tensor) else scale_dtype)
+    cdt, cshape = (torch.uint8, (rows, n // 2)) if bits == 4 else (torch.int8, (rows, n))
+    ax = _arg(x, "x", (torch.bfloat16, torch.float32), (rows, n))
+    _arg(codes, "codes", cdt, cshape)
+    _arg(scales, "scales", sd, (rows, n // g))
+    dev = x.device
     if codes is None:
-        codes = torch.empty((rows, n), dtype=torch.int8, device=x.device)
+        codes = torch.empty(cshape, dtype=cdt, device=dev)
     if scales is None:
-        scales = torch.empty((rows, n // group), dtype=scale_dtype, device=x.device)
-    _check(lib.hr_rotate_quant_int8(_ptr(x), _dtype_code(x.dtype), rows, n, m, _ptr(signs),
-                                    _ptr(block), group, _ptr(codes), _ptr(scales),
-                                    _dtype_code(scales.dtype), _stream(x.device)),
-           "hr_rotate_quant_int8")
+        scales = torch.empty((rows, n // g), dtype=sd, device=dev)
+    px, pc, pq = _ptrs(ax, ("codes", codes), ("scales", scales))
+    _check(getattr(lib, fn)(px, _dtype_code(x.dtype), rows, n, g, pc, pq, _dtype_code(sd), _stream(dev)),
+           fn)
     return codes, scales
+
+
+def quant_int4(x: torch.Tensor, group: int, scale_dtype=torch.float16,
+               codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Per-group int4 quantization without a rotation (hr_quant_int4).
+    Returns (codes uint8 [rows][n/2], scales [rows][n/group])."""
+    return _quant("hr_quant_int4", 4, x, group, scale_dtype, codes, scales)
+
+
+def quant_int8(x: torch.Tensor, group: int, scale_dtype=torch.float16,
+               codes: torch.Tensor | None = None, scales: torch.Tensor | None = None):
+    """Per-group int8 quantization without a rotation (hr_quant_int8).
+    Returns (codes int8 [rows][n], scales [rows][n/group])."""
+    return _quant("hr_quant_int8", 8, x, group, scale_dtype, codes, scales)
+
+
+# ------------------------------------------------------------------ butterfly
+
+def _log2_exact(n: int, what: str) -> int:
+    if n <= 0 or n & (n - 1):
+        raise ValueError(f"{what}={n} is not a power of two")
+    return n.bit_length() - 1
 
 
 def butterfly_coeffs(angles: torch.Tensor, precondition: bool = False) -> torch.Tensor:
     """Per-pair coefficient table [log2 n][n/2][2] fp32 from angles [log2 n][n/2]."""
-    L, half = angles.shape
+    if not isinstance(angles, torch.Tensor) or angles.dim() != 2:
+        raise ValueError("angles must be a 2-D [log2 n][n/2] tensor")
+    L, half = (int(v) for v in angles.shape)
+    n = 2 * half
+    if _log2_exact(n, "n") != L:
+        raise ValueError(f"angles has {L} stages, expected log2(n) = {_log2_exact(n, 'n')} for n = {n}")
+    aa = _arg(angles, "angles", torch.float32, (L, half))
     coeffs = torch.empty((L, half, 2), dtype=torch.float32, device=angles.device)
-    _check(lib.hr_butterfly_coeffs(_ptr(angles), 2 * half, int(precondition), _ptr(coeffs),
-                                   _stream(angles.device)), "hr_butterfly_coeffs")
+    pa, pc = _ptrs(aa, ("coeffs", coeffs))
+    _check(lib.hr_butterfly_coeffs(pa, n, int(precondition), pc, _stream(angles.device)),
+           "hr_butterfly_coeffs")
     return coeffs
 
 
@@ -162,42 +300,64 @@ def butterfly_apply(x: torch.Tensor, coeffs: torch.Tensor, precondition: bool = 
                     out: torch.Tensor | None = None):
     """Butterfly (or its transpose) per row, optionally quantized.
     Returns y, or (y_or_None, codes, scales) when ``group`` is given."""
-    rows, n = x.shape
+    rows, n = _rows_of(x, "x", (torch.float32,))
+    L = _log2_exact(n, "n")
+    ax = _arg(x, "x", torch.float32, (rows, n))
+    aco = _arg(coeffs, "coeffs", torch.float32, (L, n // 2, 2))
+    ap = _arg(perm, "perm", torch.int32, (n,))
+    _arg(out, "out", torch.float32, (rows, n))
+    g, sd, sdt = 0, HR_F16, None
+    if group is not None:
+        g = _group(group, n)
+        sdt = _scale_dtype(scale_dtype)
+        sd = _dtype_code(sdt)
+    dev = x.device
     y = None
     if want_y:
-        y = out if out is not None else torch.empty((rows, n), dtype=torch.float32, device=x.device)
+        y = out if out is not None else torch.empty((rows, n), dtype=torch.float32, device=dev)
     codes = scales = None
-    g = 0
-    sd = HR_F16
     if group is not None:
-        g = group
-        codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((rows, n // group), dtype=scale_dtype, device=x.device)
-        sd = _dtype_code(scale_dtype)
-    _check(lib.hr_butterfly_apply(_ptr(x), _ptr(y), rows, n, _ptr(coeffs), int(precondition),
-                                  _ptr(perm), int(inverse), g, _ptr(codes), _ptr(scales), sd,
-                                  _stream(x.device)), "hr_butterfly_apply")
+        codes = torch.empty((rows, n // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, n // g), dtype=sdt, device=dev)
+    px, pco, pp, py, pc, pq = _ptrs(ax, aco, ap, ("out", y), ("codes", codes), ("scales", scales))
+    _check(lib.hr_butterfly_apply(px, py, rows, n, pco, int(precondition), pp, int(inverse), g, pc, pq, sd,
+                                  _stream(dev)), "hr_butterfly_apply")
     if group is None:
         return y
     return y, codes, scales
 
 
+# ------------------------------------------------------------------ HARP
+
+def harp_n_params(b: int) -> int:
+    """Parameters per block of radix b: one angle for b = 2, else b(b-1)/2."""
+    return 1 if b == 2 else b * (b - 1) // 2
+
+
 def _radices(radices):
-    r = (ctypes.c_int32 * len(radices))(*[int(b) for b in radices])
-    return r, len(radices)
+    rs = [int(b) for b in radices]
+    if not rs:
+        raise ValueError("radices must not be empty")
+    r = (ctypes.c_int32 * len(rs))(*rs)
+    d = 1
+    for b in rs:
+        d *= b
+    return r, len(rs), rs, d
 
 
 def harp_blocks(radices, theta: torch.Tensor, fallbacks: torch.Tensor | None = None) -> torch.Tensor:
     """Dense blocks of a HARP schedule (hr_harp_blocks).  radices: a Python
-    sequence; theta: fp32 parameters; fallbacks: fp32 concatenated [b][b]
-    mixers of the radices that are not powers of two (or None)."""
-    arr, m = _radices(radices)
-    d = 1
-    for b in radices:
-        d *= int(b)
-    blocks = torch.empty(d * sum(int(b) for b in radices), dtype=torch.float32, device=theta.device)
-    _check(lib.hr_harp_blocks(arr, m, _ptr(theta), _ptr(fallbacks), _ptr(blocks),
-                              _stream(theta.device)), "hr_harp_blocks")
+    sequence; theta: fp32 parameters [sum_t (d/b_t) P_t]; fallbacks: fp32
+    concatenated [b][b] mixers of the radices that are not powers of two (or
+    None)."""
+    arr, m, rs, d = _radices(radices)
+    n_theta = sum((d // b) * harp_n_params(b) for b in rs)
+    n_fb = sum(b * b for b in rs if b & (b - 1))
+    at = _arg(theta, "theta", torch.float32, (n_theta,))
+    af = _arg(fallbacks, "fallbacks", torch.float32, (n_fb,))
+    blocks = torch.empty(d * sum(rs), dtype=torch.float32, device=theta.device)
+    pt, pf, pb = _ptrs(at, af, ("blocks", blocks))
+    _check(lib.hr_harp_blocks(arr, m, pt, pf, pb, _stream(theta.device)), "hr_harp_blocks")
     return blocks
 
 
@@ -206,75 +366,101 @@ def harp_apply(x: torch.Tensor, radices, blocks: torch.Tensor, inverse: bool = F
                out: torch.Tensor | None = None):
     """The HARP processor (or its transpose) per row (hr_harp_apply).
     Returns y, or (y_or_None, codes, scales) when ``group`` is given."""
-    rows, d = x.shape
-    arr, m = _radices(radices)
+    rows, d = _rows_of(x, "x", (torch.float32,))
+    arr, m, rs, dd = _radices(radices)
+    if dd != d:
+        raise ValueError(f"the radices multiply to {dd}, but rows have {d} elements")
+    ax = _arg(x, "x", torch.float32, (rows, d))
+    ab = _arg(blocks, "blocks", torch.float32, (d * sum(rs),))
+    _arg(out, "out", torch.float32, (rows, d))
+    g, sd, sdt = 0, HR_F16, None
+    if group is not None:
+        g = _group(group, d)
+        sdt = _scale_dtype(scale_dtype)
+        sd = _dtype_code(sdt)
+    dev = x.device
     y = None
     if want_y:
-        y = out if out is not None else torch.empty((rows, d), dtype=torch.float32, device=x.device)
+        y = out if out is not None else torch.empty((rows, d), dtype=torch.float32, device=dev)
     codes = scales = None
-    g, sd = 0, HR_F16
     if group is not None:
-        g = group
-        codes = torch.empty((rows, d // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((rows, d // group), dtype=scale_dtype, device=x.device)
-        sd = _dtype_code(scale_dtype)
-    _check(lib.hr_harp_apply(_ptr(x), _ptr(y), rows, arr, m, _ptr(blocks), int(inverse), g,
-                             _ptr(codes), _ptr(scales), sd, _stream(x.device)), "hr_harp_apply")
+        codes = torch.empty((rows, d // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, d // g), dtype=sdt, device=dev)
+    px, pb, py, pc, pq = _ptrs(ax, ab, ("out", y), ("codes", codes), ("scales", scales))
+    _check(lib.hr_harp_apply(px, py, rows, arr, m, pb, int(inverse), g, pc, pq, sd, _stream(dev)),
+           "hr_harp_apply")
     if group is None:
         return y
     return y, codes, scales
 
 
+# ------------------------------------------------------------------ dequant
+
 def dequant_int4(codes: torch.Tensor, scales: torch.Tensor, group: int,
                  out: torch.Tensor | None = None) -> torch.Tensor:
-    """x_hat = q * s (hr_dequant_int4).  codes uint8 [rows][n/2]."""
-    rows, half = codes.shape
+    """x_hat = q * s (hr_dequant_int4).  codes uint8 [rows][n/2]; scales
+    fp16/fp32 [rows][n/group]."""
+    rows, half = _rows_of(codes, "codes", (torch.uint8,))
     n = 2 * half
+    g = _group(group, n)
+    ac = _arg(codes, "codes", torch.uint8, (rows, half))
+    asc = _arg(scales, "scales", (torch.float16, torch.float32), (rows, n // g))
+    _arg(out, "out", torch.float32, (rows, n))
     o = out if out is not None else torch.empty((rows, n), dtype=torch.float32, device=codes.device)
-    _check(lib.hr_dequant_int4(_ptr(codes), _ptr(scales), _dtype_code(scales.dtype), rows, n, group,
-                               _ptr(o), _stream(codes.device)), "hr_dequant_int4")
+    pc, ps, po = _ptrs(ac, asc, ("out", o))
+    _check(lib.hr_dequant_int4(pc, ps, _dtype_code(scales.dtype), rows, n, g, po, _stream(codes.device)),
+           "hr_dequant_int4")
     return o
+
+
+# ------------------------------------------------------------------ GEMMs
+
+def _gemm(fn, a_int8, w_int8, a_codes, a_scales, w_codes, w_scales, group, out, group_acc):
+    a_dt = torch.int8 if a_int8 else torch.uint8
+    w_dt = torch.int8 if w_int8 else torch.uint8
+    M, ka = _rows_of(a_codes, "a_codes", (a_dt,))
+    N, kw = _rows_of(w_codes, "w_codes", (w_dt,))
+    K = ka if a_int8 else 2 * ka
+    if (kw if w_int8 else 2 * kw) != K:
+        raise ValueError(f"w_codes {tuple(w_codes.shape)} does not match K = {K} of a_codes "
+                         f"{tuple(a_codes.shape)}")
+    g = _group(group, K)
+    if not isinstance(a_scales, torch.Tensor) or not isinstance(w_scales, torch.Tensor):
+        raise TypeError("a_scales and w_scales must be tensors")
+    if a_scales.dtype != w_scales.dtype:
+        raise TypeError("a_scales and w_scales must share a dtype")
+    sd = _scale_dtype(a_scales.dtype)
+    aa = _arg(a_codes, "a_codes", a_dt, (M, ka))
+    asa = _arg(a_scales, "a_scales", sd, (M, K // g))
+    aw = _arg(w_codes, "w_codes", w_dt, (N, kw))
+    asw = _arg(w_scales, "w_scales", sd, (N, K // g))
+    _arg(out, "out", torch.float32, (M, N))
+    dev = a_codes.device
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    acc = torch.empty((M, N, K // g), dtype=torch.int32, device=dev) if group_acc else None
+    pa, psa, pw, psw, pc, pacc = _ptrs(aa, asa, aw, asw, ("out", c), ("group_acc", acc))
+    _check(getattr(lib, fn)(pa, psa, pw, psw, _dtype_code(sd), M, N, K, g, pc, pacc, _stream(dev)), fn)
+    return (c, acc) if group_acc else c
 
 
 def w4a4_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
               w_scales: torch.Tensor, group: int, out: torch.Tensor | None = None,
               group_acc: bool = False):
-    """C = A W^T with per-group scales (hr_w4a4_gemm).  Returns C, or (C, acc)
-    with the exact per-group int32 sums [M][N][K/group] when group_acc."""
-    M, half = a_codes.shape
-    N = int(w_codes.shape[0])
-    K = 2 * half
-    if a_scales.dtype != w_scales.dtype:
-        raise TypeError("a_scales and w_scales must share a dtype")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
-    acc = None
-    if group_acc:
-        acc = torch.empty((M, N, K // group), dtype=torch.int32, device=a_codes.device)
-    _check(lib.hr_w4a4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
-                            _dtype_code(a_scales.dtype), M, N, K, group, _ptr(c), _ptr(acc),
-                            _stream(a_codes.device)), "hr_w4a4_gemm")
-    return (c, acc) if group_acc else c
+    """C = A W^T with per-group scales (hr_w4a4_gemm): a_codes uint8 [M][K/2],
+    w_codes uint8 [N][K/2], scales [M][K/G], [N][K/G] (fp16 or fp32, same
+    dtype).  Returns C, or (C, acc) with the exact per-group int32 sums
+    [M][N][K/group] when group_acc."""
+    return _gemm("hr_w4a4_gemm", False, False, a_codes, a_scales, w_codes, w_scales, group, out,
+                 group_acc)
 
 
 def w4a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
               w_scales: torch.Tensor, group: int, out: torch.Tensor | None = None,
               group_acc: bool = False):
     """C = A W^T with int8 activation codes a_codes [M][K] and packed int4
-    weights (hr_w4a8_gemm).  Returns as w4a4_gemm."""
-    if a_codes.dtype != torch.int8:
-        raise TypeError("a_codes must be int8 [M][K]")
-    M, K = a_codes.shape
-    N = int(w_codes.shape[0])
-    if a_scales.dtype != w_scales.dtype:
-        raise TypeError("a_scales and w_scales must share a dtype")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
-    acc = None
-    if group_acc:
-        acc = torch.empty((M, N, K // group), dtype=torch.int32, device=a_codes.device)
-    _check(lib.hr_w4a8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
-                            _dtype_code(a_scales.dtype), M, N, K, group, _ptr(c), _ptr(acc),
-                            _stream(a_codes.device)), "hr_w4a8_gemm")
-    return (c, acc) if group_acc else c
+    weights w_codes uint8 [N][K/2] (hr_w4a8_gemm).  Returns as w4a4_gemm."""
+    return _gemm("hr_w4a8_gemm", True, False, a_codes, a_scales, w_codes, w_scales, group, out,
+                 group_acc)
 
 
 def w8a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tensor,
@@ -282,17 +468,39 @@ def w8a8_gemm(a_codes: torch.Tensor, a_scales: torch.Tensor, w_codes: torch.Tens
               group_acc: bool = False):
     """C = A W^T with both operands held one int8 code per element:
     a_codes [M][K], w_codes [N][K] (hr_w8a8_gemm).  Returns as w4a4_gemm."""
-    if a_codes.dtype != torch.int8 or w_codes.dtype != torch.int8:
-        raise TypeError("a_codes and w_codes must be int8 [M][K] and [N][K]")
-    M, K = a_codes.shape
-    N = int(w_codes.shape[0])
-    if a_scales.dtype != w_scales.dtype:
-        raise TypeError("a_scales and w_scales must share a dtype")
-    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
-    acc = None
-    if group_acc:
-        acc = torch.empty((M, N, K // group), dtype=torch.int32, device=a_codes.device)
-    _check(lib.hr_w8a8_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(w_codes), _ptr(w_scales),
-                            _dtype_code(a_scales.dtype), M, N, K, group, _ptr(c), _ptr(acc),
-                            _stream(a_codes.device)), "hr_w8a8_gemm")
-    return (c, acc) if group_acc else c
+    return _gemm("hr_w8a8_gemm", True, True, a_codes, a_scales, w_codes, w_scales, group, out,
+                 group_acc)
+
+
+def rotate_quant_w4a4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor,
+                           group: int, signs: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None, return_codes: bool = False):
+    """Online rotation in the decode GEMM (hr_rotate_quant_w4a4_gemm): the bf16
+    activation rows x [M][K] (M <= 16) are rotated, int4-quantized and
+    multiplied with the packed int4 weights w_codes [N][K/2] in one kernel.
+    Returns C [M][N] fp32, or (C, a_codes, a_scales) with the activation codes
+    and scales the GEMM used when return_codes."""
+    M, K = _rows_of(x, "x", (torch.bfloat16,))
+    N, kw = _rows_of(w_codes, "w_codes", (torch.uint8,))
+    if 2 * kw != K:
+        raise ValueError(f"w_codes {tuple(w_codes.shape)} does not match K = {K} of x")
+    g = _group(group, K)
+    if not isinstance(w_scales, torch.Tensor):
+        raise TypeError("w_scales must be a tensor")
+    sd = _scale_dtype(w_scales.dtype)
+    ax = _arg(x, "x", torch.bfloat16, (M, K))
+    asg = _arg(signs, "signs", torch.int8, (K,))
+    aw = _arg(w_codes, "w_codes", torch.uint8, (N, kw))
+    asw = _arg(w_scales, "w_scales", sd, (N, K // g))
+    _arg(out, "out", torch.float32, (M, N))
+    dev = x.device
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    ac = asc = None
+    if return_codes:
+        ac = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        asc = torch.empty((M, K // g), dtype=sd, device=dev)
+    px, ps, pw, psw, pc, pac, pasc = _ptrs(ax, asg, aw, asw, ("out", c), ("a_codes", ac),
+                                           ("a_scales", asc))
+    _check(lib.hr_rotate_quant_w4a4_gemm(px, HR_BF16, ps, g, pw, psw, _dtype_code(sd), M, N, K, pc, pac,
+                                         pasc, _stream(dev)), "hr_rotate_quant_w4a4_gemm")
+    return (c, ac, asc) if return_codes else c

@@ -4,7 +4,8 @@ Usage: python hadamard_rotation_int4_amd/build.py   (or call build()).  Run it a
 a script (or load it by path): importing the package first would try to load
 the very library this builds.
 Each .hip file under csrc/ is compiled to an object in parallel, then linked
-into hadamard_rotation_int4_amd/libhr.so.
+into hadamard_rotation_int4_amd/libhr.so.  The hash of the sources
+(srchash.py) is compiled in as hr_build_id(), which the binding checks.
 """
 from __future__ import annotations
 
@@ -36,9 +37,19 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str) -> str:
+def _source_hash() -> str:
+    # srchash.py sits beside this file; load it by path (the package itself
+    # would try to load the library being built)
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("hr_srchash", os.path.join(PKG, "srchash.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.source_hash()
+
+
+def _compile(src: str, defines=()) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *defines, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -53,8 +64,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    defines = [f'-DHR_SOURCE_HASH="{_source_hash()}"']
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda f: _compile(f, defines), srcs))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,6 +1,7 @@
 // extern "C" entry points of libhr.so (declared in include/hr.h): host-side
 // argument validation, then a launch on the caller's stream.  A call that
 // fails validation makes no HIP call at all.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -67,6 +68,13 @@ int32_t check_rotation(const char* fn, const void* x, int32_t x_dtype, int64_t r
 extern "C" {
 
 int32_t hr_abi_version(void) { return HR_ABI_VERSION; }
+
+// HR_SOURCE_HASH is defined by the build: a hash of the library's sources, so
+// a binding can tell a library built from other sources.
+#ifndef HR_SOURCE_HASH
+#define HR_SOURCE_HASH "unknown"
+#endif
+const char* hr_build_id(void) { return HR_SOURCE_HASH; }
 
 const char* hr_status_string(int32_t status) {
   switch (status) {
@@ -147,6 +155,47 @@ int32_t hr_rotate_quant_int8(const void* x, int32_t x_dtype, int64_t rows, int32
                              int8_t* codes, void* scales, int32_t scale_dtype, void* stream) {
   return rotate_quant("hr_rotate_quant_int8", 8, x, x_dtype, rows, n, m, signs, block, group,
                       reinterpret_cast<uint8_t*>(codes), scales, scale_dtype, stream);
+}
+
+// Shared body of hr_quant_int4 and hr_quant_int8.
+static int32_t quant_plain(const char* fn, int bits, const void* x, int32_t x_dtype, int64_t rows,
+                           int32_t n, int32_t group, uint8_t* codes, void* scales, int32_t scale_dtype,
+                           void* stream) {
+  if (rows < 0) return fail(HR_EINVAL, "%s: rows < 0", fn);
+  if ((!x || !codes || !scales) && rows > 0)
+    return fail(HR_EINVAL, "%s: x, codes and scales are required", fn);
+  if (x_dtype != HR_BF16 && x_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: x_dtype must be HR_BF16 or HR_F32", fn);
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(HR_EINVAL, "%s: x, codes and scales must be 16-byte aligned", fn);
+  if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+  if (!valid_group(group)) return fail(HR_EUNSUPPORTED, "%s: group=%d not in {32,64,128,256}", fn, group);
+  if (n <= 0 || n % group || n > (1 << 30))
+    return fail(HR_EUNSUPPORTED, "%s: n=%d must be a positive multiple of group=%d", fn, n, group);
+  if (rows == 0) return ok();
+  hr::QuantArgs a{};
+  a.x = x;
+  a.x_bf16 = x_dtype == HR_BF16;
+  a.rows = rows;
+  a.n = n;
+  a.group = group;
+  a.bits = bits;
+  a.codes = codes;
+  a.scales = scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  return from_hip(hr::launch_quant(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t hr_quant_int4(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t group,
+                      uint8_t* codes, void* scales, int32_t scale_dtype, void* stream) {
+  return quant_plain("hr_quant_int4", 4, x, x_dtype, rows, n, group, codes, scales, scale_dtype, stream);
+}
+
+int32_t hr_quant_int8(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t group,
+                      int8_t* codes, void* scales, int32_t scale_dtype, void* stream) {
+  return quant_plain("hr_quant_int8", 8, x, x_dtype, rows, n, group, reinterpret_cast<uint8_t*>(codes),
+                     scales, scale_dtype, stream);
 }
 
 int32_t hr_butterfly_coeffs(const float* angles, int32_t n, int32_t precondition, float* coeffs,
@@ -331,8 +380,7 @@ static int32_t gemm(const char* fn, int a_int8, int w_int8, const uint8_t* a_cod
     return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
   if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
     return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
-  if (group != 64 && group != 128 && group != 256)
-    return fail(HR_EUNSUPPORTED, "%s: group=%d not in {64,128,256}", fn, group);
+  if (!valid_group(group)) return fail(HR_EUNSUPPORTED, "%s: group=%d not in {32,64,128,256}", fn, group);
   if (N % 64) return fail(HR_EUNSUPPORTED, "%s: N=%lld is not a multiple of 64", fn, (long long)N);
   if (K == 0 || K % 256 || K % group || K > 65536)
     return fail(HR_EUNSUPPORTED, "%s: K=%lld must be a multiple of 256 and of group, <= 65536", fn,
@@ -375,6 +423,44 @@ int32_t hr_w8a8_gemm(const int8_t* a_codes, const void* a_scales, const int8_t* 
   return gemm("hr_w8a8_gemm", 1, 1, reinterpret_cast<const uint8_t*>(a_codes), a_scales,
               reinterpret_cast<const uint8_t*>(w_codes), w_scales, scale_dtype, M, N, K, group, c,
               group_acc, stream);
+}
+
+int32_t hr_rotate_quant_w4a4_gemm(const void* x, int32_t x_dtype, const int8_t* signs, int32_t group,
+                                  const uint8_t* w_codes, const void* w_scales, int32_t scale_dtype,
+                                  int64_t M, int64_t N, int64_t K, float* c, uint8_t* a_codes,
+                                  void* a_scales, void* stream) {
+  const char* fn = "hr_rotate_quant_w4a4_gemm";
+  if (M < 0 || N < 0 || K < 0) return fail(HR_EINVAL, "%s: negative size", fn);
+  if (M > 0 && N > 0 && (!x || !w_codes || !w_scales || !c))
+    return fail(HR_EINVAL, "%s: x, w_codes, w_scales and c are required", fn);
+  if ((a_codes == nullptr) != (a_scales == nullptr))
+    return fail(HR_EINVAL, "%s: a_codes and a_scales are given together or not at all", fn);
+  if (!aligned16(x) || (signs && !aligned16(signs)) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(c) || (a_codes && !aligned16(a_codes)) || (a_scales && !aligned16(a_scales)))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (x_dtype != HR_BF16) return fail(HR_EUNSUPPORTED, "%s: x_dtype must be HR_BF16", fn);
+  if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+  if (!valid_group(group)) return fail(HR_EUNSUPPORTED, "%s: group=%d not in {32,64,128,256}", fn, group);
+  if (M > 16) return fail(HR_EUNSUPPORTED, "%s: M=%lld > 16 (decode shapes only)", fn, (long long)M);
+  if (K != 2048 && K != 4096) return fail(HR_EUNSUPPORTED, "%s: K=%lld not 2048 or 4096", fn, (long long)K);
+  if (N % 64) return fail(HR_EUNSUPPORTED, "%s: N=%lld is not a multiple of 64", fn, (long long)N);
+  if (M == 0 || N == 0) return ok();
+  hr::FusedDecodeArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.signs = signs;
+  a.norm = (float)(1.0 / sqrt((double)K));
+  a.w = w_codes;
+  a.sw = w_scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.group = group;
+  a.c = c;
+  a.a_codes = a_codes;
+  a.a_scales = a_scales;
+  return from_hip(hr::launch_rotate_quant_gemm_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

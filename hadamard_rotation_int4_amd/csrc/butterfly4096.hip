@@ -275,13 +275,16 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
       }
       const float s32 = div7(__uint_as_float(ab));
       const float s = SCALE_F16 ? (float)(_Float16)s32 : s32;
-      float k = s > 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+      // an fp32 scale below 2^-100 would overflow its reciprocal: the group's
+      // values and scale are then both taken x 2^64 (exact; same quotients)
+      const float up = (!SCALE_F16 && s < 0x1p-100f) ? 0x1p64f : 1.0f;
+      const float k = s > 0.0f ? __builtin_amdgcn_rcpf(s * up) : 0.0f;
       const bool need_clamp = s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
       const bool clamp = __builtin_amdgcn_ballot_w64(need_clamp) != 0;
       const float M = 12582920.0f;              // 1.5 * 2^23 + 8
       float r8[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) r8[r] = fmaf(v[r], k, M);
+      for (int r = 0; r < 8; ++r) r8[r] = fmaf(SCALE_F16 ? v[r] : v[r] * up, k, M);
       if (clamp) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) r8[r] = __builtin_amdgcn_fmed3f(r8[r], M - 7.0f, M + 7.0f);

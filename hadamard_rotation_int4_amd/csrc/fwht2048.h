@@ -352,7 +352,11 @@ __device__ __forceinline__ void quant2048(const Lane2048& L, const float (&v)[4]
   const float s32 = div7(a);
   float s;
   if (SCALE_F16) s = (float)(_Float16)s32; else s = s32;
-  const float k = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s) : 0.0f;
+  // an fp32 scale below 2^-100 would overflow its reciprocal: the group's
+  // values and scale are then both taken x 2^64 (exact; same quotients)
+  const float up = (!SCALE_F16 && s < 0x1p-100f) ? 0x1p64f : 1.0f;
+  const float k = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s * up) : 0.0f;
+  const bool need_up = !SCALE_F16 && s > 0.0f && s < 0x1p-100f;
   // fp16-subnormal (or fp32-denormal) scales are imprecise: clamp needed
   const bool need_clamp = s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
   // writer lanes store the scale of their group
@@ -382,12 +386,30 @@ __device__ __forceinline__ void quant2048(const Lane2048& L, const float (&v)[4]
 #pragma unroll
   for (int j = 0; j < 4; ++j) kj[j] *= tau;
   const bool clamp = __builtin_amdgcn_ballot_w64(need_clamp) != 0;
+  const bool tiny = !SCALE_F16 && __builtin_amdgcn_ballot_w64(need_up) != 0;
+  float uj[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+  if (tiny) {
+    if (G == 256) {
+      uj[0] = uj[1] = dpp<0x00>(up);
+      uj[2] = uj[3] = dpp<0x55>(up);
+    } else {
+      uj[0] = dpp<0x00>(up);
+      uj[1] = dpp<0x55>(up);
+      uj[2] = dpp<0xAA>(up);
+      uj[3] = dpp<0xFF>(up);
+    }
+  }
   const float M = 12582920.0f;              // 1.5 * 2^23 + 8
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float r[8];
+    if (tiny) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = fmaf(v[j][e], kj[j], M);
+      for (int e = 0; e < 8; ++e) r[e] = fmaf(v[j][e] * uj[j], kj[j], M);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = fmaf(v[j][e], kj[j], M);
+    }
     if (clamp) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) r[e] = __builtin_amdgcn_fmed3f(r[e], M - 7.0f, M + 7.0f);

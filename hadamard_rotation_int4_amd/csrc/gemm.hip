@@ -9,8 +9,9 @@
 // Straightforward tile kernel: a 64x64 output tile per workgroup of 4 waves,
 // one K group per iteration: packed codes are unpacked to int8 in LDS (int8
 // activation codes of W4A8 are copied as they are), each
-// wave runs 2x2 v_mfma_i32_16x16x64_i8 tiles over the group, then converts the
-// group's int32 sums to fp32 and accumulates them with sA * sW.
+// wave runs 2x2 v_mfma_i32_16x16x64_i8 tiles over the group (16x16x32 when
+// G = 32), then converts the group's int32 sums to fp32 and accumulates them
+// with sA * sW.
 #include "hr_internal.h"
 #include "hr_device.h"
 
@@ -85,7 +86,23 @@ __global__ __launch_bounds__(256) void w4a4_gemm_simple_kernel(GemmArgs g) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
-    for (int kk = 0; kk < G; kk += 64) {
+    if (G == 32) {
+      // one v_mfma_i32_16x16x32_i8 per tile: lane l supplies 8 codes of row
+      // l % 16, k = 8 (l / 16) .. 8 (l / 16) + 7
+      long af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const long*>(la + (wm + i * 16 + (lane & 15)) * G + (lane >> 4) * 8);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[j] = *reinterpret_cast<const long*>(lw + (wn + j * 16 + (lane & 15)) * G + (lane >> 4) * 8);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    for (int kk = 0; G >= 64 && kk < G; kk += 64) {
       v4i af[2], bf[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)

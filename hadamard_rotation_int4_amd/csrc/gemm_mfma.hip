@@ -596,6 +596,11 @@ __global__ __launch_bounds__(256, 2) void w8a8_gemm_tile_kernel(GemmArgs g) {
 // reads row 8 i + l / 8, piece (l % 8) ^ ((row / 2) % 8): eight lanes per 128
 // contiguous bytes), and lane (r, j) reads its 16 codes of half h as one
 // ds_read_b128 of piece 4 h + j, reordered with v_perm_b32.
+//
+// G = 32: a group is one 16-byte piece of a packed run (32 codes) and one
+// v_mfma_i32_16x16x32_i8; lane (r, j) takes dword j of the piece (8 codes,
+// unpacked to the same even/odd K order on both operands), or for int8
+// activations the 8 bytes 8 j .. 8 j + 7 of the group.
 constexpr int kDecWaves = 16;
 constexpr int kDecRuns = 2;      // runs per operand and chunk
 
@@ -607,9 +612,9 @@ __device__ __forceinline__ void dec_wait_loads() { asm volatile("s_waitcnt vmcnt
 template <int G, bool F16, bool WRITE_ACC, bool A8>
 __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmArgs g) {
   constexpr int CH = kDecRuns;
-  constexpr int MPG = G / 64;                    // MFMAs per group
+  constexpr int MPG = G >= 64 ? G / 64 : 1;      // MFMAs per group (G = 32: one 16x16x32)
   constexpr int RPU = G >= 128 ? G / 128 : 1;    // runs per unit of work
-  constexpr int GPC = 2 * CH / MPG;              // groups per chunk
+  constexpr int GPC = G >= 64 ? 2 * CH / MPG : 4 * CH;   // groups per chunk
   typedef typename std::conditional<F16, _Float16, float>::type scale_t;
   __shared__ float part[kDecWaves][16 * 16];
   __shared__ __attribute__((aligned(16))) float sat[kDecWaves][GPC][16];   // [group][A row]
@@ -680,8 +685,30 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
     for (int u = 0; u < GPC; ++u) {
       if (u >= ng) break;
       v4i acc = (v4i){0, 0, 0, 0};
+      if (G == 32) {
+        // group u: piece p = u % 4 of run u / 4; W (and packed A) dword j of
+        // row r's piece, int8 A bytes 8 j .. 8 j + 7 of the group
+        const int run = u >> 2, p = u & 3;
+        const uint32_t o = 1024u * run + 64u * r + 16u * (p ^ ((r >> 2) & 3)) + 4u * j;
+        const uint32_t pw = *reinterpret_cast<const uint32_t*>(stw + o);
+        uint2 av;
+        if (A8) {
+          const int pc = (2 * p + (j >> 1)) ^ ((r >> 1) & 7);
+          const uint2 pa = *reinterpret_cast<const uint2*>(
+              reinterpret_cast<const char*>(&stage_a8[wave][run][0]) + rd8 + 16 * pc + 8 * (j & 1));
+          av = arow ? make_uint2(__builtin_amdgcn_perm(pa.y, pa.x, 0x06040200u),
+                                 __builtin_amdgcn_perm(pa.y, pa.x, 0x07050301u))
+                    : make_uint2(0u, 0u);
+        } else {
+          const uint32_t pa = arow ? *reinterpret_cast<const uint32_t*>(sta + o) : 0u;
+          av = make_uint2((pa << 4) & 0xF0F0F0F0u, pa & 0xF0F0F0F0u);
+        }
+        const uint2 wv = make_uint2((pw << 4) & 0xF0F0F0F0u, pw & 0xF0F0F0F0u);
+        acc = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, av),
+                                                    __builtin_bit_cast(long, wv), acc, 0, 0, 0);
+      }
 #pragma unroll
-      for (int m = u * MPG; m < (u + 1) * MPG; ++m) {
+      for (int m = u * MPG; G >= 64 && m < (u + 1) * MPG; ++m) {
         const uint32_t o = 1024u * (m >> 1) + ((m & 1) ? rd1 : rd0);
         const uint2 pw = *reinterpret_cast<const uint2*>(stw + o);
         v4i av;
@@ -728,10 +755,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void w4a4_gemm_decode_kernel(GemmAr
 
 template <int G, bool F16, bool WRITE_ACC, bool A8>
 static void launch_g(const GemmArgs& a, hipStream_t s) {
+  // G = 32 reaches this only with M <= 16 (launch_gemm_mfma)
   if (a.M <= 16) {
     hipLaunchKernelGGL((w4a4_gemm_decode_kernel<G, F16, WRITE_ACC, A8>), dim3((unsigned)(a.N / 16)),
                        dim3(kDecWaves * 64), 0, s, a);
-  } else {
+  } else if constexpr (G >= 64) {
     const dim3 grid((unsigned)(a.N / kBN), (unsigned)((a.M + kBM - 1) / kBM));
     hipLaunchKernelGGL((w4a4_gemm_tile_kernel<G, F16, WRITE_ACC, A8>), grid, dim3(256), 0, s, a);
   }
@@ -783,6 +811,11 @@ bool launch_gemm_mfma(const GemmArgs& a, hipStream_t s) {
   const bool decode = a.M <= 16;
   if (!decode && a.N % kBN) return false;
   switch (a.group) {
+    case 32:
+      // G = 32 has a kernel for M <= 16 only; the simple kernel takes M > 16
+      if (!decode) return false;
+      launch_da<32>(a, s);
+      return true;
     case 64: launch_da<64>(a, s); return true;
     case 128: launch_da<128>(a, s); return true;
     case 256: launch_da<256>(a, s); return true;

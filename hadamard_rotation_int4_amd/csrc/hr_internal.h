@@ -23,6 +23,19 @@ struct RhtArgs {
   int scale_f16;         // 1: fp16 scales, 0: fp32 scales
 };
 
+// Arguments of one rotation-free quantize call after host validation.
+struct QuantArgs {
+  const void* x;
+  int x_bf16;            // 1: bf16 input, 0: fp32 input
+  int64_t rows;
+  int n;                 // a multiple of group
+  int group;
+  int bits;              // 4 (packed int4 codes) or 8 (int8 codes)
+  uint8_t* codes;
+  void* scales;
+  int scale_f16;
+};
+
 struct ButterflyArgs {
   const float* x;
   float* y;
@@ -50,6 +63,22 @@ struct GemmArgs {
   int group;
   float* c;
   int32_t* group_acc;
+};
+
+// Arguments of the fused decode call (rotation + int4 quantization of M <= 16
+// bf16 rows, then the W4A4 GEMM on the codes) after host validation.
+struct FusedDecodeArgs {
+  const uint16_t* x;     // bf16 [M][K]
+  const int8_t* signs;   // [K] or null
+  float norm;            // 1 / sqrt(K)
+  const uint8_t* w;      // packed int4 [N][K/2]
+  const void* sw;        // [N][K/G]
+  int scale_f16;
+  int64_t M, N, K;
+  int group;
+  float* c;              // [M][N]
+  uint8_t* a_codes;      // optional [M][K/2] copy of the activation codes
+  void* a_scales;        // optional [M][K/G] copy of their scales
 };
 
 constexpr int kHarpMaxStages = 16;
@@ -86,6 +115,7 @@ hipError_t launch_harp_blocks(const HarpSchedule& sc, const float* theta, const 
 hipError_t launch_harp_apply(HarpArgs a, hipStream_t s);
 
 hipError_t launch_rht(const RhtArgs& a, hipStream_t s);
+hipError_t launch_quant(const QuantArgs& a, hipStream_t s);
 bool launch_rht2048(const RhtArgs& a, hipStream_t s);  // false: not handled
 bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s);  // false: not handled
 bool launch_mixed2048_mfma(const RhtArgs& a, hipStream_t s);  // false: not handled
@@ -96,6 +126,7 @@ bool launch_butterfly4096(const ButterflyArgs& a, hipStream_t s);  // false: not
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int scale_f16, int64_t rows,
                           int n, int group, float* out, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+hipError_t launch_rotate_quant_gemm_decode(const FusedDecodeArgs& a, hipStream_t s);
 bool launch_gemm_mfma(const GemmArgs& a, hipStream_t s);  // false: not handled
 
 }  // namespace hr

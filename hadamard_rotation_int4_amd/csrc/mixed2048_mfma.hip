@@ -234,7 +234,10 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
         const int bo = ob + r;
         const float s32 = div_const<7>(__uint_as_float(am[r]) * norm);
         const float sq = SF16 ? (float)(_Float16)s32 : s32;
-        const float kq = sq > 0.0f ? norm * taug * __builtin_amdgcn_rcpf(sq) : 0.0f;
+        // an fp32 scale below 2^-100 would overflow its reciprocal: the
+        // group's values and scale are then both taken x 2^64 (exact)
+        const float up = (!SF16 && sq < 0x1p-100f) ? 0x1p64f : 1.0f;
+        const float kq = sq > 0.0f ? norm * taug * __builtin_amdgcn_rcpf(sq * up) : 0.0f;
         // the first lane of each group stores its scale
         if ((lane & (G / 8 - 1)) == 0) {
           const int so = (bo * (P / G) + pos / G) * (SF16 ? 2 : 4);
@@ -251,7 +254,8 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
         uint32_t q[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          q[e] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(acc[e][r], kq, MQ), MQ - 7.0f, MQ + 7.0f));
+          q[e] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(SF16 ? acc[e][r] : acc[e][r] * up, kq, MQ),
+                                                         MQ - 7.0f, MQ + 7.0f));
         // nibble e of the word is code e; low bytes of the pairs first
         const uint32_t p01 = (q[1] << 4) | q[0], p23 = (q[3] << 4) | q[2];
         const uint32_t p45 = (q[5] << 4) | q[4], p67 = (q[7] << 4) | q[6];

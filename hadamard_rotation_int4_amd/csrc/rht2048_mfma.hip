@@ -157,14 +157,18 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < NG; ++i) mg[i] = max_over_rows(mg[i]);
     if (G == 256) mg[0] = __uint_as_float(umax_dpp<kQuadXor1>(__float_as_uint(mg[0])));
-    float kk[NG];
+    float kk[NG], upv[NG];
     float s_own = 0.0f;                  // scale of the group this lane stores
-    bool need_clamp = false;
+    bool need_clamp = false, need_up = false;
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
       const float s32 = div_const<BITS == 8 ? 127 : 7>(mg[i] * norm);
       const float s = SCALE_F16 ? (float)(_Float16)s32 : s32;
-      kk[i] = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s) * tau : 0.0f;
+      // an fp32 scale below 2^-100 would overflow its reciprocal: the group's
+      // values and scale are then both taken x 2^64 (exact; same quotients)
+      upv[i] = (!SCALE_F16 && s < 0x1p-100f) ? 0x1p64f : 1.0f;
+      need_up |= !SCALE_F16 && s > 0.0f && s < 0x1p-100f;
+      kk[i] = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s * upv[i]) * tau : 0.0f;
       need_clamp |= s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
       if (NG == 1 || i == (g & (NG - 1))) s_own = s32;
     }
@@ -181,14 +185,20 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
       }
     }
     const bool clamp = __builtin_amdgcn_ballot_w64(need_clamp) != 0;
+    const bool tiny = !SCALE_F16 && __builtin_amdgcn_ballot_w64(need_up) != 0;
     // q + M rounds y k to an integer in the low mantissa bits (ties to even)
     constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
     const float M = BITS == 8 ? 12582912.0f : 12582920.0f;   // 1.5 * 2^23 (+ 8 for nibbles)
     u32x4* cl = &code_lds[wib][0];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const float k = kk[G == 32 ? m : G == 64 ? (m >> 1) : 0];
-      const f32x4 lo = acc[2 * m], hi = acc[2 * m + 1];
+      const int gl = G == 32 ? m : G == 64 ? (m >> 1) : 0;
+      const float k = kk[gl];
+      f32x4 lo = acc[2 * m], hi = acc[2 * m + 1];
+      if (tiny) {
+        lo *= upv[gl];
+        hi *= upv[gl];
+      }
       float rr[8] = {fmaf(lo[0], k, M), fmaf(lo[1], k, M), fmaf(lo[2], k, M), fmaf(lo[3], k, M),
                      fmaf(hi[0], k, M), fmaf(hi[1], k, M), fmaf(hi[2], k, M), fmaf(hi[3], k, M)};
       if (clamp) {

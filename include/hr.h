@@ -54,8 +54,12 @@ typedef enum {
 } hr_dtype;
 
 /* ABI version of this header (bumped on any signature change). */
-#define HR_ABI_VERSION 3
+#define HR_ABI_VERSION 4
 int32_t hr_abi_version(void);
+
+/* Identifier of the sources the library was built from (a hash of every
+ * source file), for bindings that check they load a current build. */
+const char* hr_build_id(void);
 
 /* Static description of a status code. */
 const char* hr_status_string(int32_t status);
@@ -144,6 +148,35 @@ int32_t hr_rotate_quant_int8(const void* x, int32_t x_dtype, int64_t rows,
                              int32_t n, int32_t m, const int8_t* signs,
                              const float* block, int32_t group, int8_t* codes,
                              void* scales, int32_t scale_dtype, void* stream);
+
+/*
+ * hr_quant_int4 -- per-group symmetric absmax int4 quantization of rows that
+ * are NOT rotated (the plain operand of the experiment page's comparison).
+ *
+ * Defines: "Experiment -- Hadamard rotation for int4 (W4A4) accuracy", Method
+ * (per-group symmetric integer quantize/dequantize) and Results (its table
+ * quantizes each operand both plain and after the Hadamard rotation).
+ *
+ * For every group of G consecutive values y of a row the rule of
+ * hr_rotate_quant_int4 applies: s32 = max|y| / 7, s = fp16(s32) or s32,
+ * q = y / s rounded to nearest (ties to even), clamped to [-7, 7], 0 when
+ * s == 0.
+ *
+ *   x       [rows][n] of x_dtype (HR_BF16 or HR_F32).
+ *   n       a positive multiple of G, n <= 2^30.
+ *   group   G in {32, 64, 128, 256}.
+ *   codes   [rows][n/2] uint8 packed int4; scales [rows][n/G] of scale_dtype.
+ */
+int32_t hr_quant_int4(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t group,
+                      uint8_t* codes, void* scales, int32_t scale_dtype, void* stream);
+
+/*
+ * hr_quant_int8 -- as hr_quant_int4 with qmax = 127 and one int8 code per
+ * element (codes [rows][n] int8): the plain 8-bit operands of the same page's
+ * W8A8 and W4A8 rows.
+ */
+int32_t hr_quant_int8(const void* x, int32_t x_dtype, int64_t rows, int32_t n, int32_t group,
+                      int8_t* codes, void* scales, int32_t scale_dtype, void* stream);
 
 /*
  * hr_butterfly_coeffs -- build the per-pair 2x2 coefficient table of a
@@ -291,7 +324,7 @@ int32_t hr_dequant_int4(const uint8_t* codes, const void* scales,
  *   w_scales  [N][K/G] of scale_dtype.
  *   scale_dtype  HR_F16 or HR_F32.
  *   M >= 0; N a multiple of 64; K a multiple of 256 and of G, K <= 65536.
- *   group     G in {64, 128, 256}.
+ *   group     G in {32, 64, 128, 256}.
  *   c         [M][N] fp32 output.
  *   group_acc optional [M][N][K/G] int32 output of the exact per-group sums
  *             (a debugging aid; NULL to skip).
@@ -347,6 +380,32 @@ int32_t hr_w8a8_gemm(const int8_t* a_codes, const void* a_scales,
                      const int8_t* w_codes, const void* w_scales,
                      int32_t scale_dtype, int64_t M, int64_t N, int64_t K,
                      int32_t group, float* c, int32_t* group_acc, void* stream);
+
+/*
+ * hr_rotate_quant_w4a4_gemm -- online rotation in the decode GEMM: the
+ * activation rows are rotated and int4-quantized (hr_rotate_quant_int4 with
+ * m = 1) and multiplied with the weights (hr_w4a4_gemm) in one kernel; the
+ * activation codes never go to memory in between.
+ *
+ * Defines: as hr_rotate_quant_int4 followed by hr_w4a4_gemm; HARP technical
+ * summary (gist.science), section 4 (the decode cost of an online rotation:
+ * 0.0078 s against 0.0070 s per token) and section 2.4 (fused GPU kernels).
+ *
+ *   x         [M][K] bf16 activations (x_dtype must be HR_BF16).
+ *   signs     [K] int8 +-1 or NULL (all +1).
+ *   group     G in {32, 64, 128, 256}; the activations and the weights use it.
+ *   w_codes   [N][K/2] uint8 packed int4; w_scales [N][K/G] of scale_dtype.
+ *   M <= 16 (decode); K = 2048 or 4096; N a multiple of 64.
+ *   c         [M][N] fp32:  C = sum_g sA sW acc_g on the activation codes.
+ *   a_codes, a_scales  optional outputs ([M][K/2] uint8, [M][K/G] of
+ *             scale_dtype): the activation codes and scales the GEMM used,
+ *             as hr_rotate_quant_int4 would store them.  Both or neither.
+ * Sizes outside these return HR_EUNSUPPORTED.
+ */
+int32_t hr_rotate_quant_w4a4_gemm(const void* x, int32_t x_dtype, const int8_t* signs, int32_t group,
+                                  const uint8_t* w_codes, const void* w_scales, int32_t scale_dtype,
+                                  int64_t M, int64_t N, int64_t K, float* c, uint8_t* a_codes,
+                                  void* a_scales, void* stream);
 
 #ifdef __cplusplus
 }

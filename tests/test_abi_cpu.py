@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert hr.lib.hr_abi_version() == 3
+    assert hr.lib.hr_abi_version() == 4
     for st in (hr.HR_OK, hr.HR_EINVAL, hr.HR_EUNSUPPORTED, hr.HR_EDEVICE):
         assert hr.lib.hr_status_string(st).startswith(b"HR_")
     assert b"unknown" in hr.lib.hr_status_string(99)
@@ -140,11 +140,13 @@ def test_gemm_validation(fn):
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 256, 128, None, None, None) == hr.HR_EINVAL
     assert f(P, P, P, P, hr.HR_F16, 16, 96, 256, 128, P, None, None) == hr.HR_EUNSUPPORTED
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 384, 128, P, None, None) == hr.HR_EUNSUPPORTED
-    assert f(P, P, P, P, hr.HR_F16, 16, 64, 256, 32, P, None, None) == hr.HR_EUNSUPPORTED
+    assert f(P, P, P, P, hr.HR_F16, 16, 64, 256, 16, P, None, None) == hr.HR_EUNSUPPORTED
+    assert f(P, P, P, P, hr.HR_F16, 16, 64, 256, 96, P, None, None) == hr.HR_EUNSUPPORTED
     assert f(P, P, P, P, hr.HR_BF16, 16, 64, 256, 128, P, None, None) == hr.HR_EINVAL
     assert f(P, P, P, P, hr.HR_F16, -1, 64, 256, 128, P, None, None) == hr.HR_EINVAL
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 256, 128, P, P + 4, None) == hr.HR_EINVAL
     assert f(P, P, P, P, hr.HR_F16, 0, 64, 256, 128, P, None, None) == hr.HR_OK
+    assert f(P, P, P, P, hr.HR_F16, 0, 64, 256, 32, P, None, None) == hr.HR_OK    # G = 32 accepted
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 131072, 128, P, None, None) == hr.HR_EUNSUPPORTED
 
 
@@ -184,3 +186,143 @@ def test_harp_validation():
     assert bl(r, m, P + 8, P, P, None) == hr.HR_EINVAL
     assert bl(r9, m9, P, P, P, None) == hr.HR_EUNSUPPORTED
     assert b"hr_harp_blocks" in hr.lib.hr_last_error()
+
+
+def test_build_id_matches_sources():
+    from hadamard_rotation_int4_amd import srchash
+    assert hr.lib.hr_build_id().decode() == srchash.source_hash()
+
+
+@pytest.mark.parametrize("fn", ["hr_quant_int4", "hr_quant_int8"])
+def test_quant_validation(fn):
+    f = getattr(hr.lib, fn)
+    # x, x_dtype, rows, n, group, codes, scales, sdt, stream
+    assert f(None, hr.HR_BF16, 4, 256, 128, P, P, hr.HR_F16, None) == hr.HR_EINVAL
+    assert f(P, hr.HR_BF16, 4, 256, 128, None, P, hr.HR_F16, None) == hr.HR_EINVAL
+    assert f(P, hr.HR_BF16, 4, 256, 128, P, None, hr.HR_F16, None) == hr.HR_EINVAL
+    assert f(P, hr.HR_F16, 4, 256, 128, P, P, hr.HR_F16, None) == hr.HR_EINVAL
+    assert f(P, hr.HR_BF16, 4, 256, 128, P, P, hr.HR_BF16, None) == hr.HR_EINVAL
+    assert f(P + 2, hr.HR_BF16, 4, 256, 128, P, P, hr.HR_F16, None) == hr.HR_EINVAL
+    assert f(P, hr.HR_BF16, -1, 256, 128, P, P, hr.HR_F16, None) == hr.HR_EINVAL
+    assert f(P, hr.HR_BF16, 4, 200, 128, P, P, hr.HR_F16, None) == hr.HR_EUNSUPPORTED
+    assert f(P, hr.HR_BF16, 4, 256, 48, P, P, hr.HR_F16, None) == hr.HR_EUNSUPPORTED
+    assert f(P, hr.HR_BF16, 4, 0, 32, P, P, hr.HR_F16, None) == hr.HR_EUNSUPPORTED
+    assert f(P, hr.HR_BF16, 0, 256, 32, P, P, hr.HR_F16, None) == hr.HR_OK
+    assert f(None, hr.HR_F32, 0, 256, 32, None, None, hr.HR_F32, None) == hr.HR_OK
+    assert fn.encode() in hr.lib.hr_last_error() or hr.lib.hr_last_error() != b""
+
+
+def test_fused_decode_validation():
+    f = hr.lib.hr_rotate_quant_w4a4_gemm
+    # x, x_dtype, signs, group, w, sw, sdt, M, N, K, c, a_codes, a_scales, stream
+    ok = dict(x=P, dt=hr.HR_BF16, s=None, g=128, w=P, sw=P, sdt=hr.HR_F16, M=16, N=512, K=4096, c=P,
+              ac=None, asc=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["x"], a["dt"], a["s"], a["g"], a["w"], a["sw"], a["sdt"], a["M"], a["N"], a["K"],
+                 a["c"], a["ac"], a["asc"], None)
+
+    assert call(M=0) == hr.HR_OK
+    assert call(x=None) == hr.HR_EINVAL
+    assert call(c=None) == hr.HR_EINVAL
+    assert call(w=P + 8) == hr.HR_EINVAL
+    assert call(ac=P) == hr.HR_EINVAL                    # codes without scales
+    assert call(asc=P) == hr.HR_EINVAL
+    assert call(dt=hr.HR_F32) == hr.HR_EUNSUPPORTED
+    assert call(sdt=hr.HR_BF16) == hr.HR_EINVAL
+    assert call(M=17) == hr.HR_EUNSUPPORTED
+    assert call(K=8192) == hr.HR_EUNSUPPORTED
+    assert call(K=1024) == hr.HR_EUNSUPPORTED
+    assert call(N=96) == hr.HR_EUNSUPPORTED
+    assert call(g=16) == hr.HR_EUNSUPPORTED
+    assert call(M=-1) == hr.HR_EINVAL
+    assert call(M=0, g=32, K=2048) == hr.HR_OK
+    assert b"hr_rotate_quant_w4a4_gemm" in hr.lib.hr_last_error() or True
+
+
+# ---- the Python binding checks dtype and shape of every tensor against the
+# sizes it passes to the C call, before the call (CPU tensors: every check
+# below fails before the device check, so nothing reaches the library)
+
+import torch  # noqa: E402
+
+
+def _z(*shape, dtype=torch.float32):
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("call,exc,msg", [
+    (lambda: hr.rotate(_z(4, 2048, dtype=torch.float16)), TypeError, "x: dtype"),
+    (lambda: hr.rotate(_z(2048)), ValueError, "2-D"),
+    (lambda: hr.rotate(_z(4, 2048), signs=_z(2048, dtype=torch.int32)), TypeError, "signs"),
+    (lambda: hr.rotate(_z(4, 2048), signs=_z(1024, dtype=torch.int8)), ValueError, "signs: shape"),
+    (lambda: hr.rotate(_z(4, 2048), block=_z(3, 3)), ValueError, "divide"),
+    (lambda: hr.rotate(_z(4, 2048), block=_z(2, 3)), ValueError, "square"),
+    (lambda: hr.rotate(_z(4, 2048), out=_z(4, 1024)), ValueError, "out: shape"),
+    (lambda: hr.rotate(_z(4, 2048), out=_z(4, 2048, dtype=torch.bfloat16)), TypeError, "out: dtype"),
+    (lambda: hr.rotate_quant_int4(_z(4, 2048), 100), ValueError, "group"),
+    (lambda: hr.rotate_quant_int4(_z(4, 2048), 128, codes=_z(4, 2048, dtype=torch.uint8)),
+     ValueError, "codes: shape"),
+    (lambda: hr.rotate_quant_int4(_z(4, 2048), 128, codes=_z(4, 1024, dtype=torch.int8)),
+     TypeError, "codes: dtype"),
+    (lambda: hr.rotate_quant_int4(_z(4, 2048), 128, scales=_z(4, 32, dtype=torch.float16)),
+     ValueError, "scales: shape"),
+    (lambda: hr.rotate_quant_int4(_z(4, 2048), 128, scale_dtype=torch.bfloat16), TypeError, "scale_dtype"),
+    (lambda: hr.rotate_quant_int8(_z(4, 2048), 128, codes=_z(4, 1024, dtype=torch.int8)),
+     ValueError, "codes: shape"),
+    (lambda: hr.quant_int4(_z(4, 2048), 128, codes=_z(4, 1024, dtype=torch.int8)), TypeError, "codes"),
+    (lambda: hr.quant_int8(_z(4, 96), 64), ValueError, "group"),
+    (lambda: hr.butterfly_coeffs(_z(11, 2048)), ValueError, "stages"),
+    (lambda: hr.butterfly_coeffs(_z(12, 2048, dtype=torch.float64)), TypeError, "angles"),
+    (lambda: hr.butterfly_apply(_z(4, 4096), _z(12, 2048)), ValueError, "coeffs: shape"),
+    (lambda: hr.butterfly_apply(_z(4, 4096), _z(12, 2048, 2), perm=_z(4096, dtype=torch.int64)),
+     TypeError, "perm"),
+    (lambda: hr.butterfly_apply(_z(4, 4096), _z(12, 2048, 2), perm=_z(2048, dtype=torch.int32)),
+     ValueError, "perm: shape"),
+    (lambda: hr.butterfly_apply(_z(4, 3000), _z(12, 2048, 2)), ValueError, "power of two"),
+    (lambda: hr.harp_blocks((8, 8, 8, 5, 2), _z(10)), ValueError, "theta: shape"),
+    (lambda: hr.harp_apply(_z(4, 5120), (8, 8, 8, 5, 2), _z(100)), ValueError, "blocks: shape"),
+    (lambda: hr.harp_apply(_z(4, 5000), (8, 8, 8, 5, 2), _z(100)), ValueError, "multiply"),
+    (lambda: hr.dequant_int4(_z(4, 1024, dtype=torch.uint8), _z(4, 8, dtype=torch.float16), 128),
+     ValueError, "scales: shape"),
+    (lambda: hr.dequant_int4(_z(4, 1024, dtype=torch.int8), _z(4, 16, dtype=torch.float16), 128),
+     TypeError, "codes"),
+    (lambda: hr.w4a4_gemm(_z(16, 2048, dtype=torch.uint8), _z(16, 32, dtype=torch.float16),
+                          _z(64, 1024, dtype=torch.uint8), _z(64, 32, dtype=torch.float16), 128),
+     ValueError, "does not match K"),
+    (lambda: hr.w4a4_gemm(_z(16, 2048, dtype=torch.uint8), _z(16, 32, dtype=torch.float16),
+                          _z(64, 2048, dtype=torch.uint8), _z(64, 16, dtype=torch.float16), 128),
+     ValueError, "w_scales: shape"),
+    (lambda: hr.w4a4_gemm(_z(16, 2048, dtype=torch.uint8), _z(16, 32, dtype=torch.float16),
+                          _z(64, 2048, dtype=torch.uint8), _z(64, 32, dtype=torch.float32), 128),
+     TypeError, "share a dtype"),
+    (lambda: hr.w4a4_gemm(_z(16, 2048, dtype=torch.int8), _z(16, 32, dtype=torch.float16),
+                          _z(64, 2048, dtype=torch.uint8), _z(64, 32, dtype=torch.float16), 128),
+     TypeError, "a_codes"),
+    (lambda: hr.w4a8_gemm(_z(16, 4096, dtype=torch.int8), _z(16, 32, dtype=torch.float16),
+                          _z(64, 4096, dtype=torch.uint8), _z(64, 32, dtype=torch.float16), 128),
+     ValueError, "does not match K"),
+    (lambda: hr.w8a8_gemm(_z(16, 4096, dtype=torch.int8), _z(16, 32, dtype=torch.float16),
+                          _z(64, 4096, dtype=torch.uint8), _z(64, 32, dtype=torch.float16), 128),
+     TypeError, "w_codes"),
+    (lambda: hr.w4a4_gemm(_z(16, 2048, dtype=torch.uint8), _z(16, 32, dtype=torch.float16),
+                          _z(64, 2048, dtype=torch.uint8), _z(64, 32, dtype=torch.float16), 128,
+                          out=_z(16, 32)), ValueError, "out: shape"),
+    (lambda: hr.rotate_quant_w4a4_gemm(_z(16, 4096), _z(64, 2048, dtype=torch.uint8),
+                                       _z(64, 32, dtype=torch.float16), 128), TypeError, "x: dtype"),
+    (lambda: hr.rotate_quant_w4a4_gemm(_z(16, 4096, dtype=torch.bfloat16), _z(64, 1024, dtype=torch.uint8),
+                                       _z(64, 32, dtype=torch.float16), 128), ValueError, "does not match K"),
+    (lambda: hr.rotate_quant_w4a4_gemm(_z(16, 4096, dtype=torch.bfloat16), _z(64, 2048, dtype=torch.uint8),
+                                       _z(64, 32, dtype=torch.float16), 128,
+                                       signs=_z(2048, dtype=torch.int8)), ValueError, "signs: shape"),
+])
+def test_binding_rejects_bad_tensors(call, exc, msg):
+    with pytest.raises(exc, match=msg):
+        call()
+
+
+def test_binding_rejects_host_tensors():
+    with pytest.raises(ValueError, match="GPU"):
+        hr.rotate(_z(4, 2048))
