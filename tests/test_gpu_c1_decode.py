@@ -223,9 +223,10 @@ def test_rotate_quant_w4a4_gemm(K, G, M):
     c_ref, _, bound = oracle.gemm.w4a4_gemm(ac.cpu().numpy(), asc.cpu().numpy(), wc, sw, G,
                                             return_sums=True)
     check_gemm(c.cpu().numpy(), c_ref, bound)
-    # the call without the code outputs computes the same product
-    c2 = hr.rotate_quant_w4a4_gemm(x, _t(wc), _t(sw), G, _t(inp.signs))
-    assert torch.equal(c, c2)
+    # the call without the code outputs computes the same product, twice in a row
+    for _ in range(2):
+        c2 = hr.rotate_quant_w4a4_gemm(x, _t(wc), _t(sw), G, _t(inp.signs))
+        assert torch.equal(c, c2)
 
 
 def test_rotate_quant_w4a4_gemm_no_signs_and_zero_rows():
@@ -256,6 +257,21 @@ def test_rotate_quant_w4a4_gemm_tiny_fp32_scales():
     y64 = oracle.hadamard.rht(x, d)
     check_quant(ac.cpu().numpy(), asc.cpu().numpy(), y64, G, "f32")
     c_ref, _, bound = oracle.gemm.w4a4_gemm(ac.cpu().numpy(), asc.cpu().numpy(), gi.w_codes, sw, G,
+                                            return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound)
+
+
+@pytest.mark.parametrize("N", [64, 4096 + 64, 8192])
+def test_rotate_quant_w4a4_gemm_column_blocks(N):
+    """Few column blocks (four workgroups) and more column blocks than compute
+    units."""
+    hr = _hr()
+    inp, wc, sw = _decode_inputs(16, 2048, N, 64, 660 + N // 64, "f16")
+    c, ac, asc = hr.rotate_quant_w4a4_gemm(inp.x.to(DEV), _t(wc), _t(sw), 64, _t(inp.signs),
+                                           return_codes=True)
+    y64 = oracle.hadamard.rht(inp.x.float().numpy(), inp.signs)
+    check_quant(ac.cpu().numpy(), asc.cpu().numpy(), y64, 64, "f16")
+    c_ref, _, bound = oracle.gemm.w4a4_gemm(ac.cpu().numpy(), asc.cpu().numpy(), wc, sw, 64,
                                             return_sums=True)
     check_gemm(c.cpu().numpy(), c_ref, bound)
 
