@@ -76,21 +76,26 @@ class Timing(float):
 
 def _timed(fn, steps, warmup, nbuf=1):
     """Run fn(i) warmup + steps times on the current stream (the stream the
-    library launches on).  HIP events bracket every timed launch: the mean is
-    the whole timed region over the number of launches, the median and the
-    minimum come from the per-launch intervals.  Returns a Timing (ms)."""
+    library launches on).  HIP events bracket the timed launches: the mean is
+    the whole timed region over the number of launches.  The region is cut
+    into batches of at least 10 launches by one event each (an event between
+    every launch would add about 2 us to each); the median and the minimum are
+    over the per-launch means of those batches.  Returns a Timing (ms)."""
     import torch
     for i in range(warmup):
         fn(i % nbuf)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    nb = min(20, max(1, steps // 10))
+    cuts = [round(k * steps / nb) for k in range(nb + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
     ev[0].record()
-    for i in range(steps):
-        fn(i % nbuf)
-        ev[i + 1].record()
+    for b in range(nb):
+        for i in range(cuts[b], cuts[b + 1]):
+            fn(i % nbuf)
+        ev[b + 1].record()
     torch.cuda.synchronize()
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-    return Timing(ev[0].elapsed_time(ev[steps]) / steps, float(np.median(per)), float(per.min()))
+    per = np.array([ev[b].elapsed_time(ev[b + 1]) / (cuts[b + 1] - cuts[b]) for b in range(nb)])
+    return Timing(ev[0].elapsed_time(ev[nb]) / steps, float(np.median(per)), float(per.min()))
 
 
 def _timed_graph(fn, steps, warmup, per_graph=20, nbuf=1):

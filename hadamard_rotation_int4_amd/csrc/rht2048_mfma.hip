@@ -28,7 +28,14 @@
 
 namespace hr {
 
+// Workgroups (of four waves) per CU: three for the quantizing 2048-point
+// instances (36 KB of LDS each; 61.9 us against 65.0 us with two, same box,
+// bf16 65536 x 2048, G = 128), two for the fp32 output and the 4096-point
+// rows, whose 68 KB would not fit three times, and one for the fp32 output of
+// 4096-point rows (its registers leave room for one wave per SIMD).
 constexpr int kMfmaBlocksPerCu = 2;
+template <bool OUT_F32, int CH>
+constexpr int mfma_blocks_per_cu() { return (OUT_F32 && CH == 2) ? 1 : (OUT_F32 || CH == 2) ? 2 : 3; }
 
 // 16-byte global -> LDS copy (the builtin sits in a device function: used
 // directly in a kernel template it can cost the instance its host stub)
@@ -37,7 +44,7 @@ __device__ __forceinline__ void mfma_lds_load16(const void* gp, void* lp) {
 }
 
 template <int G, bool SCALE_F16, bool OUT_F32, int BITS, int CH = 1>
-__global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
+__global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2048_mfma_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ signs, int64_t rows,
     float* __restrict__ yout, uint8_t* __restrict__ codes, void* __restrict__ scales, float norm) {
   static_assert(CH == 1 || CH == 2, "rows of one or two 2048-point chunks");
@@ -144,33 +151,74 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
       mr[m] = fmaxf(m2, m3);
     }
     constexpr int NG = G == 32 ? 4 : G == 64 ? 2 : 1;   // groups per lane (shared by its 4 rows)
-    float mg[NG];
-    if (G == 32) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) mg[m] = mr[m];
-    } else if (G == 64) {
-      mg[0] = fmaxf(mr[0], mr[1]);
-      mg[NG - 1] = fmaxf(mr[2], mr[3]);
-    } else {
-      mg[0] = fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3]));
-    }
-#pragma unroll
-    for (int i = 0; i < NG; ++i) mg[i] = max_over_rows(mg[i]);
-    if (G == 256) mg[0] = __uint_as_float(umax_dpp<kQuadXor1>(__float_as_uint(mg[0])));
     float kk[NG], upv[NG];
     float s_own = 0.0f;                  // scale of the group this lane stores
     bool need_clamp = false, need_up = false;
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const float s32 = div_const<BITS == 8 ? 127 : 7>(mg[i] * norm);
+    if constexpr (G == 32 || G == 64) {
+      // Reduce-scatter over the lanes q, q + 16, q + 32, q + 48 (rows of the
+      // same DPP position): permlane16 swaps pair rows 0/1 and 2/3, permlane32
+      // pairs the halves, and lane row g ends with the absmax of group g % NG
+      // of its block -- the group whose scale it stores.  The scale arithmetic
+      // runs once per lane, and swaps in the opposite order give every lane
+      // the multipliers of all NG groups.
+      float own;
+      if (G == 32) {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(mr[0]), __float_as_uint(mr[1]), false, false);
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(mr[2]), __float_as_uint(mr[3]), false, false);
+        const float pm = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        const float qm = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm), __float_as_uint(qm), false, false);
+        own = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+      } else {
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(fmaxf(mr[0], mr[1])),
+                                                        __float_as_uint(fmaxf(mr[2], mr[3])), false, false);
+        const float pm = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm), __float_as_uint(pm), false, false);
+        own = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+      }
+      const float s32 = div_const<BITS == 8 ? 127 : 7>(own * norm);
       const float s = SCALE_F16 ? (float)(_Float16)s32 : s32;
       // an fp32 scale below 2^-100 would overflow its reciprocal: the group's
       // values and scale are then both taken x 2^64 (exact; same quotients)
-      upv[i] = (!SCALE_F16 && s < 0x1p-100f) ? 0x1p64f : 1.0f;
-      need_up |= !SCALE_F16 && s > 0.0f && s < 0x1p-100f;
-      kk[i] = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s * upv[i]) * tau : 0.0f;
-      need_clamp |= s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
-      if (NG == 1 || i == (g & (NG - 1))) s_own = s32;
+      const float up = (!SCALE_F16 && s < 0x1p-100f) ? 0x1p64f : 1.0f;
+      need_up = !SCALE_F16 && s > 0.0f && s < 0x1p-100f;
+      const float k = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s * up) * tau : 0.0f;
+      need_clamp = s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
+      s_own = s32;
+      auto gather = [&](float v, float (&out)[NG]) {
+        if constexpr (G == 32) {
+          const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+          const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+          const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+          out[0] = __uint_as_float(a[0]);
+          out[1] = __uint_as_float(a[1]);
+          out[2] = __uint_as_float(b[0]);
+          out[3] = __uint_as_float(b[1]);
+        } else {
+          const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+          out[0] = __uint_as_float(a[0]);
+          out[NG - 1] = __uint_as_float(a[1]);
+        }
+      };
+      gather(k, kk);
+      if (!SCALE_F16) gather(up, upv);
+      else {
+#pragma unroll
+        for (int i = 0; i < NG; ++i) upv[i] = 1.0f;
+      }
+    } else {
+      float mg = fmaxf(fmaxf(mr[0], mr[1]), fmaxf(mr[2], mr[3]));
+      mg = max_over_rows(mg);
+      if (G == 256) mg = __uint_as_float(umax_dpp<kQuadXor1>(__float_as_uint(mg)));
+      const float s32 = div_const<BITS == 8 ? 127 : 7>(mg * norm);
+      const float s = SCALE_F16 ? (float)(_Float16)s32 : s32;
+      // an fp32 scale below 2^-100 would overflow its reciprocal: the group's
+      // values and scale are then both taken x 2^64 (exact; same quotients)
+      upv[0] = (!SCALE_F16 && s < 0x1p-100f) ? 0x1p64f : 1.0f;
+      need_up = !SCALE_F16 && s > 0.0f && s < 0x1p-100f;
+      kk[0] = s > 0.0f ? norm * __builtin_amdgcn_rcpf(s * upv[0]) * tau : 0.0f;
+      need_clamp = s > 0.0f && s < (SCALE_F16 ? 6.103515625e-05f : 1.17549435e-38f);
+      s_own = s32;
     }
     {
       int64_t si = -1;
@@ -272,7 +320,7 @@ __global__ __launch_bounds__(256, kMfmaBlocksPerCu) void rht2048_mfma_kernel(
 template <int G, bool SCALE_F16, bool OUT_F32, int BITS = 4>
 static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
   int64_t blocks = (a.rows + 3) / 4;              // 4 waves per block, one row per wave
-  const int64_t cap = 256 * kMfmaBlocksPerCu;
+  const int64_t cap = 256 * (a.p == 4096 ? mfma_blocks_per_cu<OUT_F32, 2>() : mfma_blocks_per_cu<OUT_F32, 1>());
   if (blocks > cap) blocks = cap;
   if (a.p == 4096)
     hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS, 2>), dim3((unsigned)blocks),
