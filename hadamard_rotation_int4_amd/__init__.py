@@ -23,6 +23,7 @@ from . import srchash
 __all__ = ["HRError", "rotate", "rotate_quant_int4", "rotate_quant_int8", "quant_int4", "quant_int8",
            "butterfly_coeffs", "butterfly_apply", "harp_blocks", "harp_apply", "harp_n_params",
            "dequant_int4", "w4a4_gemm", "w4a8_gemm", "w8a8_gemm", "rotate_quant_w4a4_gemm",
+           "fp6_rows", "w4a4_to_fp6", "w4a4_gemm_fp6",
            "lib", "LIB_PATH", "SYMBOLS",
            "HR_OK", "HR_EINVAL", "HR_EUNSUPPORTED", "HR_EDEVICE", "HR_F32", "HR_BF16", "HR_F16"]
 
@@ -54,6 +55,8 @@ SYMBOLS = {
     "hr_w8a8_gemm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "hr_rotate_quant_w4a4_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _vp,
                                          _vp, _vp, _vp]),
+    "hr_w4a4_to_fp6": (_i32, [_vp, _vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "hr_w4a4_gemm_fp6": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
 }
 
 
@@ -504,3 +507,77 @@ def rotate_quant_w4a4_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: tor
     _check(lib.hr_rotate_quant_w4a4_gemm(px, HR_BF16, ps, g, pw, psw, _dtype_code(sd), M, N, K, pc, pac,
                                          pasc, _stream(dev)), "hr_rotate_quant_w4a4_gemm")
     return (c, ac, asc) if return_codes else c
+
+
+def fp6_rows(rows: int) -> int:
+    """Rows of a tiled fp6 operand of `rows` rows (panels of 128)."""
+    return (rows + 127) // 128 * 128
+
+
+def w4a4_to_fp6(codes: torch.Tensor, scales: torch.Tensor | None = None, group: int | None = None,
+                out: torch.Tensor | None = None, out_scales: torch.Tensor | None = None):
+    """Packed int4 codes [rows][K/2] (and their scales [rows][K/G]) -> the
+    tiled fp6 operand format of hr_w4a4_gemm_fp6 (hr_w4a4_to_fp6): the tiles
+    as a [fp6_rows(rows)][K*3/4] uint8 tensor, and, with scales, the scales
+    transposed to [K/G][fp6_rows(rows)].  Returns the tiles, or (tiles,
+    scales) when scales are given."""
+    rows, half = _rows_of(codes, "codes", (torch.uint8,))
+    K = 2 * half
+    if K % 128:
+        raise ValueError(f"K={K} is not a multiple of 128")
+    P = fp6_rows(rows)
+    ac = _arg(codes, "codes", torch.uint8, (rows, half))
+    _arg(out, "out", torch.uint8, (P, K * 3 // 4))
+    o = out if out is not None else torch.empty((P, K * 3 // 4), dtype=torch.uint8, device=codes.device)
+    if scales is None:
+        if group is not None or out_scales is not None:
+            raise ValueError("group and out_scales go with scales")
+        pc, po = _ptrs(ac, ("out", o))
+        _check(lib.hr_w4a4_to_fp6(pc, None, 0, rows, K, 0, po, None, _stream(codes.device)), "hr_w4a4_to_fp6")
+        return o
+    if not isinstance(scales, torch.Tensor):
+        raise TypeError("scales must be a tensor")
+    if group not in (128, 256) or K % group:
+        raise ValueError(f"group={group} must be 128 or 256 and divide K={K}")
+    sd = _scale_dtype(scales.dtype)
+    asc = _arg(scales, "scales", sd, (rows, K // group))
+    _arg(out_scales, "out_scales", sd, (K // group, P))
+    os_ = out_scales if out_scales is not None else torch.empty((K // group, P), dtype=sd, device=codes.device)
+    pc, ps, po, pos = _ptrs(ac, asc, ("out", o), ("out_scales", os_))
+    _check(lib.hr_w4a4_to_fp6(pc, ps, _dtype_code(sd), rows, K, group, po, pos, _stream(codes.device)),
+           "hr_w4a4_to_fp6")
+    return o, os_
+
+
+def w4a4_gemm_fp6(a_f6: torch.Tensor, a_scales: torch.Tensor, w_f6: torch.Tensor,
+                  w_scales: torch.Tensor, group: int, M: int, out: torch.Tensor | None = None,
+                  group_acc: bool = False):
+    """C = A W^T on operands in the tiled fp6 format (hr_w4a4_gemm_fp6), as
+    w4a4_to_fp6 writes them: a_f6 [fp6_rows(M)][K*3/4] and a_scales
+    [K/G][fp6_rows(M)] for the M activation rows, w_f6 [N][K*3/4] and w_scales
+    [K/G][N] for the N weight rows.  Returns as w4a4_gemm."""
+    if not isinstance(a_scales, torch.Tensor) or not isinstance(w_scales, torch.Tensor):
+        raise TypeError("a_scales and w_scales must be tensors")
+    if a_scales.dtype != w_scales.dtype:
+        raise TypeError("a_scales and w_scales must share a dtype")
+    if not isinstance(M, int) or M < 0:
+        raise ValueError(f"M={M} must be a non-negative int")
+    N, kw = _rows_of(w_f6, "w_f6", (torch.uint8,))
+    _, ka = _rows_of(a_f6, "a_f6", (torch.uint8,))
+    if ka % 3 or kw != ka:
+        raise ValueError(f"a_f6 {tuple(a_f6.shape)} and w_f6 {tuple(w_f6.shape)} are not [.][K*3/4]")
+    K = ka * 4 // 3
+    g = _group(group, K)
+    sd = _scale_dtype(a_scales.dtype)
+    aa = _arg(a_f6, "a_f6", torch.uint8, (fp6_rows(M), ka))
+    asa = _arg(a_scales, "a_scales", sd, (K // g, fp6_rows(M)))
+    aw = _arg(w_f6, "w_f6", torch.uint8, (N, kw))
+    asw = _arg(w_scales, "w_scales", sd, (K // g, N))
+    _arg(out, "out", torch.float32, (M, N))
+    dev = a_f6.device
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=dev)
+    acc = torch.empty((M, N, K // g), dtype=torch.int32, device=dev) if group_acc else None
+    pa, psa, pw, psw, pc, pacc = _ptrs(aa, asa, aw, asw, ("out", c), ("group_acc", acc))
+    _check(lib.hr_w4a4_gemm_fp6(pa, psa, pw, psw, _dtype_code(sd), M, N, K, g, pc, pacc, _stream(dev)),
+           "hr_w4a4_gemm_fp6")
+    return (c, acc) if group_acc else c

@@ -463,4 +463,59 @@ int32_t hr_rotate_quant_w4a4_gemm(const void* x, int32_t x_dtype, const int8_t* 
   return from_hip(hr::launch_rotate_quant_gemm_decode(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+int32_t hr_w4a4_to_fp6(const uint8_t* codes, const void* scales, int32_t scale_dtype, int64_t rows, int64_t K,
+                       int32_t group, uint8_t* out, void* out_scales, void* stream) {
+  const char* fn = "hr_w4a4_to_fp6";
+  if (rows < 0 || K < 0) return fail(HR_EINVAL, "%s: negative size", fn);
+  if (rows > 0 && K > 0 && (!codes || !out)) return fail(HR_EINVAL, "%s: codes and out are required", fn);
+  if (!scales != !out_scales) return fail(HR_EINVAL, "%s: scales and out_scales go together", fn);
+  if (!aligned16(codes) || !aligned16(out) || !aligned16(scales) || !aligned16(out_scales))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (K % 128 || K > (int64_t(1) << 30))
+    return fail(HR_EUNSUPPORTED, "%s: K=%lld must be a multiple of 128", fn, (long long)K);
+  if (scales) {
+    if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+      return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+    if ((group != 128 && group != 256) || K % group)
+      return fail(HR_EUNSUPPORTED, "%s: group=%d must be 128 or 256 and divide K", fn, group);
+  }
+  if (rows == 0 || K == 0) return ok();
+  return from_hip(hr::launch_int4_to_fp6(codes, scales, scale_dtype == HR_F16, rows, K, group, out, out_scales,
+                                         static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+int32_t hr_w4a4_gemm_fp6(const uint8_t* a_f6, const void* a_scales, const uint8_t* w_f6, const void* w_scales,
+                         int32_t scale_dtype, int64_t M, int64_t N, int64_t K, int32_t group, float* c,
+                         int32_t* group_acc, void* stream) {
+  const char* fn = "hr_w4a4_gemm_fp6";
+  if (M < 0 || N < 0 || K < 0) return fail(HR_EINVAL, "%s: negative size", fn);
+  if (M > 0 && N > 0 && (!a_f6 || !a_scales || !w_f6 || !w_scales || !c))
+    return fail(HR_EINVAL, "%s: a_f6, a_scales, w_f6, w_scales and c are required", fn);
+  if (!aligned16(a_f6) || !aligned16(a_scales) || !aligned16(w_f6) || !aligned16(w_scales) || !aligned16(c) ||
+      (group_acc && !aligned16(group_acc)))
+    return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+  if (group != 128 && group != 256)
+    return fail(HR_EUNSUPPORTED, "%s: group=%d not in {128,256}", fn, group);
+  if (N % 128) return fail(HR_EUNSUPPORTED, "%s: N=%lld is not a multiple of 128", fn, (long long)N);
+  if (K == 0 || K % group || K > 65536)
+    return fail(HR_EUNSUPPORTED, "%s: K=%lld must be a multiple of group, <= 65536", fn, (long long)K);
+  if (M == 0 || N == 0) return ok();
+  hr::GemmArgs a{};
+  a.a = a_f6;
+  a.sa = a_scales;
+  a.w = w_f6;
+  a.sw = w_scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.group = group;
+  a.c = c;
+  a.group_acc = group_acc;
+  return from_hip(hr::launch_gemm_fp6(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 }  // extern "C"

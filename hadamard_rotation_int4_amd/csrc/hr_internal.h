@@ -126,6 +126,11 @@ bool launch_butterfly4096(const ButterflyArgs& a, hipStream_t s);  // false: not
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int scale_f16, int64_t rows,
                           int n, int group, float* out, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// scales may be null (then out_scales, scale_f16 and group are unused)
+hipError_t launch_int4_to_fp6(const uint8_t* codes, const void* scales, bool scale_f16, int64_t rows, int64_t K,
+                              int group, uint8_t* out, void* out_scales, hipStream_t s);
+// a.a, a.w: tiled fp6; a.sa, a.sw: transposed scales [K / G][padded rows]
+hipError_t launch_gemm_fp6(const GemmArgs& a, hipStream_t s);
 hipError_t launch_rotate_quant_gemm_decode(const FusedDecodeArgs& a, hipStream_t s);
 bool launch_gemm_mfma(const GemmArgs& a, hipStream_t s);  // false: not handled
 

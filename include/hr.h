@@ -382,6 +382,55 @@ int32_t hr_w8a8_gemm(const int8_t* a_codes, const void* a_scales,
                      int32_t group, float* c, int32_t* group_acc, void* stream);
 
 /*
+ * hr_w4a4_to_fp6 -- packed int4 codes (and their scales) to the tiled fp6
+ * operand format that hr_w4a4_gemm_fp6 reads: the same codes and scales, held
+ * where the fp6 matrix cores and the GEMM's copies take them.
+ *
+ * Defines: the operands of "Experiment -- Hadamard rotation for int4 (W4A4)
+ * accuracy", Hypothesis (int4 codes on a same-precision MAC).
+ *
+ * A code q in [-8, 7] becomes the fp6 e2m3 field (q < 0) << 5 | |q| (the value
+ * q / 8; exact).  A slot is 32 consecutive codes of a row in 24 bytes, code
+ * 32 j + e (e < 32) of the slot in bits 6 e .. 6 e + 5 of its 192-bit
+ * little-endian value.  Rows go in panels of 128, the last panel padded with
+ * zero rows (P = ceil(rows / 128) * 128 rows in all); K goes in blocks of 128
+ * codes (slots 0-3 of the block).  Panel p, block b is a 12288-byte tile at
+ * ((p * K / 128) + b) * 12288; in it, slots h and h + 2 (h = 0, 1) of the
+ * panel's row r are the 48 bytes at h * 6144 + r * 48.
+ *
+ *   codes       [rows][K/2] uint8 packed int4 (see conventions).
+ *   out         P * K * 3 / 4 bytes.
+ *   scales      [rows][K/G] of scale_dtype (HR_F16 or HR_F32), or NULL.
+ *   out_scales  [K/G][P] of scale_dtype: scales transposed, zeros for the
+ *               padding rows; NULL exactly when scales is.
+ *   K           a multiple of 128; group G in {128, 256} dividing K (only read
+ *               with scales).
+ * All pointers 16-byte aligned.
+ */
+int32_t hr_w4a4_to_fp6(const uint8_t* codes, const void* scales, int32_t scale_dtype, int64_t rows, int64_t K,
+                       int32_t group, uint8_t* out, void* out_scales, void* stream);
+
+/*
+ * hr_w4a4_gemm_fp6 -- the W4A4 GEMM of hr_w4a4_gemm on operands in the tiled
+ * fp6 format of hr_w4a4_to_fp6, on v_mfma_f32_32x32x64_f8f6f4.
+ *
+ * Defines: as hr_w4a4_gemm ("Experiment -- Hadamard rotation for int4 (W4A4)
+ * accuracy", Hypothesis and Verdict).  The same sums and scale fusion: every
+ * fp6 product of two codes is exact and so is the fp32 sum of a group, so
+ * acc[m][n][g] is the exact integer group sum and C matches hr_w4a4_gemm.
+ *
+ *   a_f6, a_scales  activation codes of M rows and their transposed scales,
+ *                   as hr_w4a4_to_fp6 writes them (ceil(M / 128) panels).
+ *   w_f6, w_scales  weight codes of N rows and scales, the same way.
+ *   scale_dtype, c, group_acc: as hr_w4a4_gemm.
+ *   M >= 0; N a multiple of 128; K a multiple of G, K <= 65536.
+ *   group     G in {128, 256}.
+ */
+int32_t hr_w4a4_gemm_fp6(const uint8_t* a_f6, const void* a_scales, const uint8_t* w_f6, const void* w_scales,
+                         int32_t scale_dtype, int64_t M, int64_t N, int64_t K, int32_t group, float* c,
+                         int32_t* group_acc, void* stream);
+
+/*
  * hr_rotate_quant_w4a4_gemm -- online rotation in the decode GEMM: the
  * activation rows are rotated and int4-quantized (hr_rotate_quant_int4 with
  * m = 1) and multiplied with the weights (hr_w4a4_gemm) in one kernel; the

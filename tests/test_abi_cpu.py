@@ -150,6 +150,29 @@ def test_gemm_validation(fn):
     assert f(P, P, P, P, hr.HR_F16, 16, 64, 131072, 128, P, None, None) == hr.HR_EUNSUPPORTED
 
 
+def test_fp6_validation():
+    conv, gemm = hr.lib.hr_w4a4_to_fp6, hr.lib.hr_w4a4_gemm_fp6
+    # codes, scales, sdt, rows, K, group, out, out_scales, stream
+    assert conv(None, None, 0, 4, 256, 0, P, None, None) == hr.HR_EINVAL
+    assert conv(P, None, 0, 4, 256, 0, P + 8, None, None) == hr.HR_EINVAL
+    assert conv(P, None, 0, -1, 256, 0, P, None, None) == hr.HR_EINVAL
+    assert conv(P, None, 0, 4, 192, 0, P, None, None) == hr.HR_EUNSUPPORTED   # K not a multiple of 128
+    assert conv(P, P, hr.HR_F16, 4, 256, 128, P, None, None) == hr.HR_EINVAL   # scales without out_scales
+    assert conv(P, P, hr.HR_BF16, 4, 256, 128, P, P, None) == hr.HR_EINVAL
+    assert conv(P, P, hr.HR_F16, 4, 256, 64, P, P, None) == hr.HR_EUNSUPPORTED
+    assert conv(P, P, hr.HR_F16, 4, 384, 256, P, P, None) == hr.HR_EUNSUPPORTED
+    assert conv(P, None, 0, 0, 256, 0, P, None, None) == hr.HR_OK
+    assert conv(P, P, hr.HR_F32, 0, 256, 256, P, P, None) == hr.HR_OK
+    # a, sa, w, sw, sdt, M, N, K, group, c, acc, stream
+    assert gemm(None, P, P, P, hr.HR_F16, 16, 128, 256, 128, P, None, None) == hr.HR_EINVAL
+    assert gemm(P, P, P, P, hr.HR_BF16, 16, 128, 256, 128, P, None, None) == hr.HR_EINVAL
+    assert gemm(P, P, P, P, hr.HR_F16, 16, 64, 256, 128, P, None, None) == hr.HR_EUNSUPPORTED   # N % 128
+    assert gemm(P, P, P, P, hr.HR_F16, 16, 128, 256, 64, P, None, None) == hr.HR_EUNSUPPORTED   # G
+    assert gemm(P, P, P, P, hr.HR_F16, 16, 128, 384, 256, P, None, None) == hr.HR_EUNSUPPORTED  # K % G
+    assert gemm(P, P, P, P, hr.HR_F16, 16, 128, 131072, 128, P, None, None) == hr.HR_EUNSUPPORTED
+    assert gemm(P, P, P, P, hr.HR_F16, 0, 128, 384, 128, P, None, None) == hr.HR_OK
+
+
 def _rad(*b):
     return (ctypes.c_int32 * len(b))(*b), len(b)
 

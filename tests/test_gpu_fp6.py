@@ -1,0 +1,152 @@
+"""GPU parity of the fp6 path (hr_w4a4_to_fp6, hr_w4a4_gemm_fp6) against the
+oracle, through the C ABI.  The tiled format is decoded here from its
+definition: a slot is 32 codes of a row in 24 bytes, code 32 j + e of the slot
+in bits 6 e .. 6 e + 5 of its 192-bit little-endian value, field = (q < 0) << 5
+| |q|; panel p (128 rows), block b (128 codes) is the 12288-byte tile at
+(p * K / 128 + b) * 12288, holding slots h and h + 2 of the panel's row r at
+h * 6144 + r * 48 + 24 * (slot // 2)."""
+import numpy as np
+import pytest
+import torch
+
+import hr_inputs
+import oracle
+from parity import check_gemm
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _hr():
+    import hadamard_rotation_int4_amd as hr
+    return hr
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def decode_fp6_tiles(f6: np.ndarray, rows: int) -> np.ndarray:
+    """Tiled fp6 bytes [padded rows][K*3/4] -> int codes [padded rows][K]
+    (from the format definition); checks every field is a valid code."""
+    prow, nb = f6.shape
+    K = nb * 4 // 3
+    flat = f6.reshape(-1)
+    out = np.empty((prow, K), dtype=np.int64)
+    for r in range(prow):
+        p, rr = divmod(r, 128)
+        for j in range(K // 32):
+            b, sl = divmod(j, 4)
+            at = (p * (K // 128) + b) * 12288 + (sl & 1) * 6144 + rr * 48 + (sl >> 1) * 24
+            bits = int.from_bytes(flat[at:at + 24].tobytes(), "little")
+            for e in range(32):
+                f = (bits >> (6 * e)) & 0x3F
+                assert f & 0x10 == 0 and (f & 0x0F) <= 8, (r, j, e, f)
+                out[r, 32 * j + e] = -(f & 0x0F) if f & 0x20 else (f & 0x0F)
+    return out
+
+
+def _all_nibble_codes(rng, rows, K):
+    """Packed codes with every nibble pattern, -8 included."""
+    return rng.integers(0, 256, size=(rows, K // 2), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("rows,K", [(1, 128), (5, 256), (130, 384), (33, 4096)])
+def test_int4_to_fp6_matches_codes(rows, K):
+    """Every code lands in its place in the tiles; padding rows are zeros
+    (the output buffer starts as 0xFF bytes, so nothing is left unwritten)."""
+    hr = _hr()
+    codes = _all_nibble_codes(np.random.default_rng(rows + K), rows, K)
+    out = torch.full((hr.fp6_rows(rows), K * 3 // 4), 255, dtype=torch.uint8, device=DEV)
+    f6 = hr.w4a4_to_fp6(_t(codes), out=out).cpu().numpy()
+    assert f6.shape == ((rows + 127) // 128 * 128, K * 3 // 4)
+    dec = decode_fp6_tiles(f6, rows)
+    np.testing.assert_array_equal(dec[:rows], oracle.quant.unpack_int4(codes).astype(np.int64))
+    assert not dec[rows:].any()
+
+
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+@pytest.mark.parametrize("rows,K,G", [(1, 128, 128), (130, 768, 256), (257, 1024, 128)])
+def test_int4_to_fp6_scales(dtype, rows, K, G):
+    """The scales come out transposed to [K/G][padded rows], bit for bit, with
+    zeros in the padding rows; the tiles match the codes-only call."""
+    hr = _hr()
+    rng = np.random.default_rng(rows + K + G)
+    codes = _all_nibble_codes(rng, rows, K)
+    sc = (rng.random((rows, K // G)) + 0.01).astype(dtype)
+    P = hr.fp6_rows(rows)
+    o_s = torch.full((K // G, P), 7.0, dtype=torch.float16 if dtype == np.float16 else torch.float32, device=DEV)
+    f6, st = hr.w4a4_to_fp6(_t(codes), _t(sc), G, out_scales=o_s)
+    ref = np.zeros((K // G, P), dtype=dtype)
+    ref[:, :rows] = sc.T
+    np.testing.assert_array_equal(st.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+    assert torch.equal(f6, hr.w4a4_to_fp6(_t(codes)))
+
+
+def _gemm_case(M, N, K, G, seed, scale_mode, all_nibbles=False):
+    gi = hr_inputs.gemm_inputs(M=M, N=N, K=K, group=G, seed=seed)
+    a, w = gi.a_codes, gi.w_codes
+    if all_nibbles:
+        rng = np.random.default_rng(seed)
+        a, w = _all_nibble_codes(rng, M, K), _all_nibble_codes(rng, N, K)
+    sa, sw = gi.a_scales, gi.w_scales
+    if scale_mode == "f32":
+        sa, sw = sa.astype(np.float32), sw.astype(np.float32)
+    return a, w, sa, sw
+
+
+@pytest.mark.parametrize("G", [128, 256])
+@pytest.mark.parametrize("M", [1, 130, 256])
+@pytest.mark.parametrize("scale_mode", ["f16", "f32"])
+def test_gemm_fp6_parity(G, M, scale_mode):
+    hr = _hr()
+    N, K = 256, 1024
+    a, w, sa, sw = _gemm_case(M, N, K, G, 800 + M + G, scale_mode, all_nibbles=(M == 130))
+    (a6, st_a), (w6, st_w) = hr.w4a4_to_fp6(_t(a), _t(sa), G), hr.w4a4_to_fp6(_t(w), _t(sw), G)
+    c, acc = hr.w4a4_gemm_fp6(a6, st_a, w6, st_w, G, M, group_acc=True)
+    c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(a, sa, w, sw, G, return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
+    c2 = hr.w4a4_gemm_fp6(a6, st_a, w6, st_w, G, M)
+    assert torch.equal(c, c2)
+
+
+@pytest.mark.parametrize("K,G", [(128, 128), (384, 128), (640, 128), (512, 256), (1280, 256)])
+def test_gemm_fp6_stage_counts(K, G):
+    """K from one stage up, through every remainder of the three-stage
+    pipeline (and of six stages for G = 256)."""
+    hr = _hr()
+    M, N = 70, 128
+    a, w, sa, sw = _gemm_case(M, N, K, G, 860 + K + G, "f16", all_nibbles=True)
+    (a6, st_a), (w6, st_w) = hr.w4a4_to_fp6(_t(a), _t(sa), G), hr.w4a4_to_fp6(_t(w), _t(sw), G)
+    c, acc = hr.w4a4_gemm_fp6(a6, st_a, w6, st_w, G, M, group_acc=True)
+    c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(a, sa, w, sw, G, return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
+
+
+def test_gemm_fp6_long_k():
+    """K = 65536 (the largest accepted): 512 groups per output."""
+    hr = _hr()
+    a, w, sa, sw = _gemm_case(64, 128, 65536, 128, 840, "f16", all_nibbles=True)
+    (a6, st_a), (w6, st_w) = hr.w4a4_to_fp6(_t(a), _t(sa), 128), hr.w4a4_to_fp6(_t(w), _t(sw), 128)
+    c, acc = hr.w4a4_gemm_fp6(a6, st_a, w6, st_w, 128, 64, group_acc=True)
+    c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(a, sa, w, sw, 128, return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
+
+
+def test_gemm_fp6_4096_sampled():
+    """The 4096^3 G = 128 workload: every output of 48 sampled rows (and the
+    first and last) against the oracle, and the whole product against the int8
+    kernel's within the GEMM tolerance."""
+    hr = _hr()
+    gi = hr_inputs.gemm_inputs(M=4096)
+    a6, st_a = hr.w4a4_to_fp6(_t(gi.a_codes), _t(gi.a_scales), 128)
+    w6, st_w = hr.w4a4_to_fp6(_t(gi.w_codes), _t(gi.w_scales), 128)
+    c = hr.w4a4_gemm_fp6(a6, st_a, w6, st_w, 128, 4096)
+    rows = np.unique(np.concatenate([np.random.default_rng(850).choice(4096, 48, replace=False), [0, 4095]]))
+    c_ref, _, bound = oracle.gemm.w4a4_gemm(gi.a_codes, gi.a_scales, gi.w_codes, gi.w_scales, 128, rows=rows,
+                                            return_sums=True)
+    check_gemm(c[torch.from_numpy(rows).to(DEV)].cpu().numpy(), c_ref, bound)
+    c8 = hr.w4a4_gemm(_t(gi.a_codes), _t(gi.a_scales), _t(gi.w_codes), _t(gi.w_scales), 128)
+    diff = (c - c8).abs().max().item()
+    assert diff <= 1e-5 * float(np.abs(bound).max()), diff
