@@ -24,6 +24,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA peak
+FP6_PEAK_TOPS = 10100.0        # MI355X dense fp6 / fp4 MFMA peak
 METRIC = "fused RHT+int4 quant GB/s (% of HBM peak) at K=2048; W4A4 GEMM int8 TOPS"
 
 ROWS, N, GROUP = 65536, 2048, 128
@@ -271,6 +272,10 @@ def main(argv=None):
                                         (hr.w4a8_gemm, t(g8.a_codes), t(g8.a_scales))):
             for _ in range(args.steps):
                 call(a_codes, a_scales, wd, swd, 128, out=cg)
+        a6, sta = hr.w4a4_to_fp6(t(gi.a_codes), t(gi.a_scales), 128)
+        w6, stw = hr.w4a4_to_fp6(wd, swd, 128)
+        for _ in range(args.steps):
+            hr.w4a4_gemm_fp6(a6, sta, w6, stw, 128, 4096, out=cg)
         torch.cuda.synchronize()
         return 0
 
@@ -295,11 +300,21 @@ def main(argv=None):
         torch.cuda.synchronize()
         return 0
 
-    ms = _timed(step, args.steps, args.warmup, nbuf)
+    # the timed steps are replays of a HIP graph of 20 launches (K a multiple
+    # of 20; else of 10, else eager launches): the host then stays far ahead
+    # of the GPU, so a pause of the Python process cannot leave the GPU idle
+    # inside the timed region
+    pg = 20 if args.steps % 20 == 0 else 10 if args.steps % 10 == 0 else 1
+    if pg > 1:
+        ms = _timed_graph(step, args.steps, args.warmup, per_graph=pg, nbuf=nbuf)
+        how = f"HIP graph of {pg} launches over {nbuf} buffer sets, replayed {args.steps // pg} times"
+    else:
+        ms = _timed(step, args.steps, args.warmup, nbuf)
+        how = "eager launches"
     alg = rht_alg_bytes(ROWS, N, GROUP)
     gbs = alg / (ms * 1e-3) / 1e9
     kernels = {"rht_quant_bf16_65536x2048_g128": _entry(ms, **{"GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                                                               "bytes": alg})}
+                                                               "bytes": alg, "timing": how})}
 
     def hbm_entry(t, byts, **kw):
         return _entry(t, **{"GB/s": byts / t / 1e6, "frac_hbm": byts / t / 1e6 / HBM_PEAK_GBS,
@@ -394,7 +409,24 @@ def main(argv=None):
         msg = _timed(lambda i: hr.w4a4_gemm(ad, sad, wd, swd, 128, out=cg), args.steps, args.warmup)
         kernels["w4a4_gemm_4096x4096x4096_g128"] = gemm_entry(
             msg, 4096, 4096 * 2048 * 2 + 8192 * 32 * 2 + 4096 * 4096 * 4, timing="eager launches")
-        del ad, sad, cg
+        # the same product on fp6 matrix cores: weights converted once (as a
+        # model would at load time); "gemm" times the GEMM on converted
+        # operands, "with_a_convert" adds the per-call activation conversion
+        a6, sta = hr.w4a4_to_fp6(ad, sad, 128)
+        w6, stw = hr.w4a4_to_fp6(wd, swd, 128)
+        b6 = 2 * 4096 * 3072 + 8192 * 32 * 2 + 4096 * 4096 * 4
+        ms6 = _timed(lambda i: hr.w4a4_gemm_fp6(a6, sta, w6, stw, 128, 4096, out=cg), args.steps, args.warmup)
+        kernels["w4a4_gemm_fp6_4096x4096x4096_g128"] = gemm_entry(
+            ms6, 4096, b6, timing="eager launches", operands="tiled fp6 (hr_w4a4_to_fp6)")
+
+        def conv_gemm(i):
+            hr.w4a4_to_fp6(ad, sad, 128, out=a6, out_scales=sta)
+            hr.w4a4_gemm_fp6(a6, sta, w6, stw, 128, 4096, out=cg)
+        ms6c = _timed(conv_gemm, args.steps, args.warmup)
+        kernels["w4a4_gemm_fp6_with_a_convert_4096x4096x4096_g128"] = gemm_entry(
+            ms6c, 4096, b6 + 4096 * 2048 + 4096 * 32 * 2 + 4096 * 3072 + 4096 * 32 * 2, timing="eager launches",
+            operands="packed int4 activations converted per call, weights converted once")
+        del ad, sad, cg, a6, sta, w6, stw
 
         # decode shapes (M = 16): a call is shorter than the Python call that
         # issues it, so calls are captured in a HIP graph and replayed.  "hot":
@@ -505,6 +537,11 @@ def main(argv=None):
     if g4096:
         out["w4a4_gemm_tops"] = round(g4096["TOPS"], 1)
         out["w4a4_gemm_frac_int8_peak"] = round(g4096["frac_int8_peak"], 4)
+    g6 = kernels.get("w4a4_gemm_fp6_4096x4096x4096_g128")
+    if g6:
+        out["w4a4_gemm_fp6_tops"] = round(g6["TOPS"], 1)
+        out["w4a4_gemm_fp6_frac_int8_peak"] = round(g6["frac_int8_peak"], 4)
+        out["w4a4_gemm_fp6_frac_fp6_peak"] = round(g6["TOPS"] / FP6_PEAK_TOPS, 4)
     out["ms_per_step_median"] = round(ms.median, 5)
     out["ms_per_step_min"] = round(ms.min, 5)
     out["kernels"] = {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -78,40 +78,43 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
     }
   };
   // B operands of one row from stage st: lane (q, g) takes slot 64 s + 16 g +
-  // A(q) of each chunk for K-step s.  One asm block waits for the stage (at
-  // most 4 CH younger vector-memory ops, the other stage's loads, may still be
-  // pending; loads complete in order) and for its own results.
+  // A(q) of each chunk for K-step s.  First a wait for the stage's loads:
+  // vector-memory operations complete in issue order (loads and stores
+  // alike), so it is a wait until at most `younger` operations are
+  // outstanding, where younger counts what this wave issued after the
+  // stage's loads -- the next row's loads and the stores of the rows
+  // processed since (see the loop).  Then one asm block reads the stage and
+  // waits for its own results.
   const uint32_t rd_lane = 16u * (uint32_t)(16 * g + a4);
-  auto read_stage = [&](int st, bool next_pending, u32x4 (&b)[CH][4]) {
-    const uint32_t addr = (uint32_t)(uintptr_t)&stage_lds[wib][st][0] + rd_lane;
-#define HR_DSR4(WAIT)                                                                    \
-    asm volatile(WAIT "\n\t"                                                             \
-                 "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"             \
-                 "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t" \
-                 "s_waitcnt lgkmcnt(0)"                                                  \
-                 : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3])             \
-                 : "v"(addr)                                                             \
-                 : "memory")
-#define HR_DSR8(WAIT)                                                                    \
-    asm volatile(WAIT "\n\t"                                                             \
-                 "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"             \
-                 "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t" \
-                 "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t" \
-                 "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t" \
-                 "s_waitcnt lgkmcnt(0)"                                                  \
-                 : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3]),            \
-                   "=v"(b[CH - 1][0]), "=v"(b[CH - 1][1]), "=v"(b[CH - 1][2]), "=v"(b[CH - 1][3]) \
-                 : "v"(addr)                                                             \
-                 : "memory")
-    if (CH == 1) {
-      if (next_pending) HR_DSR4("s_waitcnt vmcnt(4)");
-      else HR_DSR4("s_waitcnt vmcnt(0)");
-    } else {
-      if (next_pending) HR_DSR8("s_waitcnt vmcnt(8)");
-      else HR_DSR8("s_waitcnt vmcnt(0)");
+  auto read_stage = [&](int st, int younger, u32x4 (&b)[CH][4]) {
+    // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+    // left at their maxima (no wait)
+    switch (younger) {
+#define HR_VMW(V) \
+      case V: __builtin_amdgcn_s_waitcnt(((V) & 15) | (((V) >> 4) << 14) | 0x0F70); break;
+      HR_VMW(0) HR_VMW(2) HR_VMW(3) HR_VMW(4) HR_VMW(6) HR_VMW(7) HR_VMW(8) HR_VMW(10)
+      HR_VMW(12) HR_VMW(14) HR_VMW(16) HR_VMW(20) HR_VMW(24) HR_VMW(32) HR_VMW(40)
+#undef HR_VMW
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // vmcnt(0)
     }
-#undef HR_DSR4
-#undef HR_DSR8
+    const uint32_t addr = (uint32_t)(uintptr_t)&stage_lds[wib][st][0] + rd_lane;
+    if (CH == 1)
+      asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+                   "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3])
+                   : "v"(addr)
+                   : "memory");
+    else
+      asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+                   "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
+                   "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
+                   "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+                   "s_waitcnt lgkmcnt(0)"
+                   : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3]),
+                     "=v"(b[CH - 1][0]), "=v"(b[CH - 1][1]), "=v"(b[CH - 1][2]), "=v"(b[CH - 1][3])
+                   : "v"(addr)
+                   : "memory");
   };
 
   // outputs of chunk ch of a row: acc[T][v] = tau * Y[a4][c] of the chunk,
@@ -306,12 +309,22 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
     emit(row, 1, dif);
   };
 
+  // Vector-memory operations per processed row (every wave issues each of
+  // them: the scale-storing lanes are in every wave): one code store per
+  // chunk (two for int8) and one scale store, or eight fp32 stores per chunk
+  constexpr int SPR = CH * (OUT_F32 ? 8 : (BITS == 8 ? 2 : 1) + 1);
+  constexpr int LPR = 4 * CH;      // loads per row
   int64_t row = wave;
   if (row < rows) issue(row, 0);
   if (row + nwaves < rows) issue(row + nwaves, 1);
-  for (int st = 0; row < rows; row += nwaves, st ^= 1) {
+  for (int st = 0, it = 0; row < rows; row += nwaves, st ^= 1, ++it) {
     u32x4 b[CH][4];
-    read_stage(st, row + nwaves < rows, b);
+    // issued after this row's loads: the next row's loads (if any; issued
+    // before this row's loads only in the prologue), and the stores of the
+    // rows processed since this row's loads were issued (none, one, then two)
+    const bool next = row + nwaves < rows;
+    const int younger = (next ? LPR : 0) + (it == 0 ? 0 : it == 1 ? SPR : 2 * SPR);
+    read_stage(st, younger, b);
     if (row + 2 * nwaves < rows) issue(row + 2 * nwaves, st);
     process(row, b);
   }
