@@ -575,6 +575,7 @@ GEMM_COUNTER_PASSES = (
     "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES",
     "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY "
     "SQ_ACTIVE_INST_ANY SQ_INSTS_SALU SQ_INSTS_VMEM_RD",
+    "TA_TA_BUSY_sum TD_TD_BUSY_sum TCC_HIT_sum TCC_MISS_sum GRBM_GUI_ACTIVE",
 )
 
 
@@ -588,7 +589,7 @@ def _summarize_counters(d, prefix, kernels, out_name, title, run_flag):
         return
     lines = [f"# rocprofv3 --pmc counters, per dispatch, of {title}",
              f"# command, one per pass: rocprofv3 --pmc <pass> -d <dir>/{prefix}<i> -o run --output-format csv "
-             f"-- python bench.py {run_flag} --steps 10"]
+             f"-- python3 bench.py {run_flag} --steps 10"]
     for i, pmc in enumerate(GEMM_COUNTER_PASSES, 1):
         lines.append(f"# pass {i}: {pmc}")
     for label, name in kernels:
@@ -614,13 +615,21 @@ def _summarize_counters(d, prefix, kernels, out_name, title, run_flag):
         wv = vals.get("SQ_WAVES")
         if wv and va:
             lines.append(f"  VALU instructions per wave = {va / wv:.1f}")
+        # GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles; TA_TA_BUSY_sum the 256 CUs' texture addressers
+        ga, ta = vals.get("GRBM_GUI_ACTIVE"), vals.get("TA_TA_BUSY_sum")
+        if ga and ta:
+            lines.append(f"  TA busy cycles per CU / GPU busy cycles = {(ta / 256) / (ga / 8):.3f}")
+        th, tm = vals.get("TCC_HIT_sum"), vals.get("TCC_MISS_sum")
+        if th is not None and tm:
+            lines.append(f"  L2 hit rate = {th / (th + tm):.3f}")
     with open(os.path.join(PROFILES, out_name), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
 def _summarize_gemm_counters(d):
     _summarize_counters(d, "gemm_p", (("W4A4", "w4a4_gemm_tile_kernel<128, true, false, false>"),
-                                      ("W4A8", "w4a4_gemm_tile_kernel<128, true, false, true>")),
+                                      ("W4A8", "w4a4_gemm_tile_kernel<128, true, false, true>"),
+                                      ("W4A4 on fp6 matrix cores", "w4a4_gemm_fp6_tile_kernel<128, true, false>")),
                         "w4a4_w4a8_gemm_4096_g128.counters.txt",
                         "the 4096^3 G=128 fp16-scale GEMM tile kernels", "--profile-gemm")
 
@@ -638,8 +647,8 @@ def summarize_profile(d):
     os.makedirs(PROFILES, exist_ok=True)
     stats = _read_csv(os.path.join(d, "ktrace", "**", "*kernel_stats.csv"))
     lines = ["# rocprofv3 --kernel-trace --stats summary (times in microseconds)",
-             "# command: rocprofv3 --kernel-trace --stats -d <dir>/ktrace -o run -- "
-             "python bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+             "# command: rocprofv3 --kernel-trace --stats -d <dir>/ktrace -o run --output-format csv -- "
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
              "kernel | calls | avg_us | min_us | max_us | total_%"]
     for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
         lines.append(" | ".join([r["Name"][:110], r["Calls"],
@@ -662,8 +671,8 @@ def summarize_profile(d):
             break
     out = {"kernel": MAIN_KERNEL_NAME, "workload": "bf16 65536x2048, G=128, fp16 scales",
            "source_hash": main_kernel_hash(),
-           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir>/fetch -o run -- "
-                      "python bench.py --profile-run --steps 20",
+           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -d <dir>/fetch (<dir>/write) -o run "
+                      "--output-format csv -- python3 bench.py --profile-run --steps 20",
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": nk,
            "copy_kernel_match": copy_kernel, "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf,
            "copy_write_kib": cw, "copy_dispatches": nc}

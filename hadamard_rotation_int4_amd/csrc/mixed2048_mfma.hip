@@ -238,6 +238,11 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
         // group's values and scale are then both taken x 2^64 (exact)
         const float up = (!SF16 && sq < 0x1p-100f) ? 0x1p64f : 1.0f;
         const float kq = sq > 0.0f ? norm * taug * __builtin_amdgcn_rcpf(sq * up) : 0.0f;
+        // the clamp and the x 2^64 only where some group of the wave needs
+        // them (a wave-uniform branch)
+        const bool clamp = __builtin_amdgcn_ballot_w64(
+                               sq > 0.0f && sq < (SF16 ? 6.103515625e-05f : 1.17549435e-38f)) != 0;
+        const bool tiny = !SF16 && __builtin_amdgcn_ballot_w64(sq > 0.0f && sq < 0x1p-100f) != 0;
         // the first lane of each group stores its scale
         if ((lane & (G / 8 - 1)) == 0) {
           const int so = (bo * (P / G) + pos / G) * (SF16 ? 2 : 4);
@@ -251,11 +256,16 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
         // to [-7, 7] only acts for fp16-subnormal (or fp32-denormal) scales,
         // whose reciprocal is imprecise; elsewhere |y k| rounds to at most 7.
         constexpr float MQ = 12582920.0f;
+        float qf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[e] = fmaf(tiny ? acc[e][r] * up : acc[e][r], kq, MQ);
+        if (clamp) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[e] = __builtin_amdgcn_fmed3f(qf[e], MQ - 7.0f, MQ + 7.0f);
+        }
         uint32_t q[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          q[e] = __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(SF16 ? acc[e][r] : acc[e][r] * up, kq, MQ),
-                                                         MQ - 7.0f, MQ + 7.0f));
+        for (int e = 0; e < 8; ++e) q[e] = __float_as_uint(qf[e]);
         // nibble e of the word is code e; low bytes of the pairs first
         const uint32_t p01 = (q[1] << 4) | q[0], p23 = (q[3] << 4) | q[2];
         const uint32_t p45 = (q[5] << 4) | q[4], p67 = (q[7] << 4) | q[6];
