@@ -11,7 +11,7 @@
 // global_load_lds (kBfRing rows in flight per CU without holding registers):
 // wave w loads bytes 2048 w .. 2048 w + 2047 of a row, which are exactly the
 // 8-element slices of its own 64 threads, so a wave waits only for its own
-// loads.  With codes only, the next row is prefetched into registers.  Each
+// loads.  With codes only, the next two rows are prefetched into registers.  Each
 // thread owns 8 elements of the row per pass; the 12 stages run as 4 passes of 3
 // register stages.  In pass k the thread's 8 registers are the elements whose
 // index bits 3k..3k+2 take all 8 values, the other 9 bits being the thread
@@ -131,55 +131,8 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
   // thread t's elements 8t .. 8t+7: bytes 32 t of the stage
   const uint32_t rd_off = 32u * (uint32_t)t;
 
-  int st = 0, iter = 0;
-  f32x4 p0, p1;       // register prefetch of the next row (without the ring)
-  if (!RING && (int64_t)blockIdx.x < rows) {
-    const f32x4* xr = reinterpret_cast<const f32x4*>(x + (int64_t)blockIdx.x * N) + 2 * t;
-    p0 = __builtin_nontemporal_load(xr);
-    p1 = __builtin_nontemporal_load(xr + 1);
-  }
-  for (int64_t row = blockIdx.x; row < rows;
-       row += step, st = st + 1 == kBfRing ? 0 : st + 1, ++iter) {
-    float v[8];
-    if (!RING) {
-      v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
-      v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
-      if (row + step < rows) {
-        const f32x4* xr = reinterpret_cast<const f32x4*>(x + (row + step) * N) + 2 * t;
-        p0 = __builtin_nontemporal_load(xr);
-        p1 = __builtin_nontemporal_load(xr + 1);
-      }
-    } else {
-      // wait for this row's two loads.  Vector memory operations complete in
-      // issue order; the ones issued after them are the younger rows' loads (two
-      // each) and the stores of the rows processed since: SU per row, two fp32
-      // stores and the code and scale stores.  Every wave issues each of them
-      // (a wave's 64 threads always include scale-storing ones, since G / 8 <= 32),
-      // so the count is exact.  Near the end of the rows everything is drained.
-      f32x4 n0, n1;
-      const uint32_t addr = (uint32_t)(uintptr_t)&ring[st][0] + rd_off;
-      constexpr int SU = (OUT_Y ? 2 : 0) + (G > 0 ? 2 : 0);
-#define HR_BFR(N)                                                                            \
-      asm volatile("s_waitcnt vmcnt(" #N ")\n\tds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\t" \
-                   "s_waitcnt lgkmcnt(0)"                                                     \
-                   : "=v"(n0), "=v"(n1)                                                       \
-                   : "v"(addr)                                                                \
-                   : "memory")
-      static_assert(kBfRing == 3, "the wait counts below assume three ring stages");
-      if (row + (kBfRing - 1) * step < rows) {
-        const int done = iter < kBfRing ? iter : kBfRing;   // rows processed whose stores are younger
-        static_assert(SU == 2 || SU == 4, "fp32 out, codes, or both");
-        if (done == 0) HR_BFR(4);
-        else if (SU == 2) { if (done == 1) HR_BFR(6); else if (done == 2) HR_BFR(8); else HR_BFR(10); }
-        else { if (done == 1) HR_BFR(8); else if (done == 2) HR_BFR(12); else HR_BFR(16); }
-      } else {
-        HR_BFR(0);
-      }
-#undef HR_BFR
-      v[0] = n0.x; v[1] = n0.y; v[2] = n0.z; v[3] = n0.w;
-      v[4] = n1.x; v[5] = n1.y; v[6] = n1.z; v[7] = n1.w;
-      if (row + kBfRing * step < rows) issue(row + kBfRing * step, st);
-    }
+  // the row's transform, gather and outputs, from the thread's 8 elements v
+  auto body = [&](int64_t row, float (&v)[8]) {
     if (!INVERSE) {
       // pass 0: stages 0, 1, 2 on elements 8t .. 8t+7
 #pragma unroll
@@ -294,6 +247,74 @@ __global__ __launch_bounds__(kBfThreads4096, 1) void butterfly4096_kernel(
         const int64_t si = row * (N / G) + (8 * t) / G;
         if (SCALE_F16) reinterpret_cast<_Float16*>(scales)[si] = (_Float16)s32;
         else reinterpret_cast<float*>(scales)[si] = s32;
+      }
+    }
+  };
+
+  if (RING) {
+    int st = 0, iter = 0;
+    for (int64_t row = blockIdx.x; row < rows; row += step, st = st + 1 == kBfRing ? 0 : st + 1, ++iter) {
+      float v[8];
+      // wait for this row's two loads.  Vector memory operations complete in
+      // issue order; the ones issued after them are the younger rows' loads (two
+      // each) and the stores of the rows processed since: SU per row, two fp32
+      // stores and the code and scale stores.  Every wave issues each of them
+      // (a wave's 64 threads always include scale-storing ones, since G / 8 <= 32),
+      // so the count is exact.  Near the end of the rows everything is drained.
+      f32x4 n0, n1;
+      const uint32_t addr = (uint32_t)(uintptr_t)&ring[st][0] + rd_off;
+      constexpr int SU = (OUT_Y ? 2 : 0) + (G > 0 ? 2 : 0);
+#define HR_BFR(N)                                                                            \
+      asm volatile("s_waitcnt vmcnt(" #N ")\n\tds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:16\n\t" \
+                   "s_waitcnt lgkmcnt(0)"                                                     \
+                   : "=v"(n0), "=v"(n1)                                                       \
+                   : "v"(addr)                                                                \
+                   : "memory")
+      static_assert(kBfRing == 3, "the wait counts below assume three ring stages");
+      if (row + (kBfRing - 1) * step < rows) {
+        const int done = iter < kBfRing ? iter : kBfRing;   // rows processed whose stores are younger
+        static_assert(SU == 2 || SU == 4, "fp32 out, codes, or both");
+        if (done == 0) HR_BFR(4);
+        else if (SU == 2) { if (done == 1) HR_BFR(6); else if (done == 2) HR_BFR(8); else HR_BFR(10); }
+        else { if (done == 1) HR_BFR(8); else if (done == 2) HR_BFR(12); else HR_BFR(16); }
+      } else {
+        HR_BFR(0);
+      }
+#undef HR_BFR
+      v[0] = n0.x; v[1] = n0.y; v[2] = n0.z; v[3] = n0.w;
+      v[4] = n1.x; v[5] = n1.y; v[6] = n1.z; v[7] = n1.w;
+      if (row + kBfRing * step < rows) issue(row + kBfRing * step, st);
+      body(row, v);
+    }
+  } else {
+    // register prefetch two rows deep, in two register sets used in turn (a
+    // copy from one set to the other would wait for the younger load).  The
+    // loads are unconditional: past the last row a set reloads a row already
+    // held (never used), so that no register merges loaded and unloaded values
+    auto load = [&](int64_t r, f32x4& q0, f32x4& q1) {
+      const f32x4* xr = reinterpret_cast<const f32x4*>(x + r * N) + 2 * t;
+      q0 = __builtin_nontemporal_load(xr);
+      q1 = __builtin_nontemporal_load(xr + 1);
+    };
+    auto take = [&](const f32x4& q0, const f32x4& q1, float (&v)[8]) {
+      v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+      v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+    };
+    const int64_t r0 = blockIdx.x;
+    if (r0 < rows) {
+      f32x4 a0, a1, b0, b1;
+      load(r0, a0, a1);
+      load(r0 + step < rows ? r0 + step : r0, b0, b1);
+      for (int64_t row = r0; row < rows; row += 2 * step) {
+        float v[8];
+        take(a0, a1, v);
+        load(row + 2 * step < rows ? row + 2 * step : row, a0, a1);
+        body(row, v);
+        if (row + step >= rows) break;
+        float w[8];
+        take(b0, b1, w);
+        load(row + 3 * step < rows ? row + 3 * step : row, b0, b1);
+        body(row + step, w);
       }
     }
   }
