@@ -648,7 +648,7 @@ def summarize_profile(d):
     stats = _read_csv(os.path.join(d, "ktrace", "**", "*kernel_stats.csv"))
     lines = ["# rocprofv3 --kernel-trace --stats summary (times in microseconds)",
              "# command: rocprofv3 --kernel-trace --stats -d <dir>/ktrace -o run --output-format csv -- "
-             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+             "python3 bench.py --no-cpu-baseline",
              "kernel | calls | avg_us | min_us | max_us | total_%"]
     for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
         lines.append(" | ".join([r["Name"][:110], r["Calls"],
