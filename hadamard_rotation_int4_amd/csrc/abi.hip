@@ -473,6 +473,8 @@ int32_t hr_w4a4_to_fp6(const uint8_t* codes, const void* scales, int32_t scale_d
     return fail(HR_EINVAL, "%s: pointers must be 16-byte aligned", fn);
   if (K % 128 || K > (int64_t(1) << 30))
     return fail(HR_EUNSUPPORTED, "%s: K=%lld must be a multiple of 128", fn, (long long)K);
+  if (rows > int64_t(128) * 65535)
+    return fail(HR_EUNSUPPORTED, "%s: rows=%lld above 128 * 65535", fn, (long long)rows);
   if (scales) {
     if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
       return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);

@@ -55,60 +55,65 @@ __device__ __forceinline__ uint64_t f6_fields8(uint32_t x) {
   return (uint64_t)lo | ((uint64_t)hi << 24);
 }
 
-// one thread per slot: 16 bytes of packed codes in (zeros for the padding
-// rows of the last panel), 24 bytes out at the slot's place in its tile; then
-// the scales, if any, transposed to [group][padded row] (zeros for padding)
+// One workgroup of 256 threads per output tile (panel p = blockIdx.y, block
+// kb = blockIdx.x): thread t writes row r = t % 128 of plane h = t / 128, the
+// 48 contiguous bytes of slots h and h + 2 of that row's block (zeros for the
+// padding rows of the last panel), so a wave writes 3 KB of the tile in one
+// run.  The tile holding a group's first codes also writes the panel's 128
+// transposed scales of that group.
 template <typename S>
-__global__ __launch_bounds__(256) void int4_to_fp6_kernel(const uint4* __restrict__ codes, int64_t rows,
-                                                         int64_t K, uint2* __restrict__ out,
-                                                         const S* __restrict__ scales, int64_t ngroups,
+__global__ __launch_bounds__(256) void int4_to_fp6_kernel(const uint8_t* __restrict__ codes, int64_t rows,
+                                                         int64_t K, uint8_t* __restrict__ out,
+                                                         const S* __restrict__ scales, int group,
                                                          S* __restrict__ out_scales) {
-  const int64_t spr = K / 32;                        // slots per row
-  const int64_t prow = (rows + 127) / 128 * 128;
-  const int64_t total = prow * spr;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (int64_t i = first; i < total; i += stride) {
-    const int64_t row = i / spr, j = i % spr;
-    const uint4 x = row < rows ? codes[i] : make_uint4(0u, 0u, 0u, 0u);
+  const int t = threadIdx.x;
+  const int r = t & 127, h = t >> 7;
+  const int64_t p = blockIdx.y, kb = blockIdx.x;
+  const int64_t row = p * 128 + r;
+  const int64_t nkb = K / 128;
+  uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
+  if (row < rows) {
+    // slots h and h + 2 of the block: packed bytes 16 h and 16 (h + 2) of its 64
+    const uint4* src = reinterpret_cast<const uint4*>(codes + row * (K / 2) + kb * 64);
+    x0 = src[h];
+    x1 = src[h + 2];
+  }
+  auto fields = [](const uint4& x, uint32_t (&o)[6]) {
     const uint64_t f0 = f6_fields8(x.x), f1 = f6_fields8(x.y), f2 = f6_fields8(x.z), f3 = f6_fields8(x.w);
     // 192 bits: f0 | f1 << 48 | f2 << 96 | f3 << 144
-    const uint32_t o0 = (uint32_t)f0;
-    const uint32_t o1 = (uint32_t)(f0 >> 32) | ((uint32_t)f1 << 16);
-    const uint32_t o2 = (uint32_t)(f1 >> 16);
-    const uint32_t o3 = (uint32_t)f2;
-    const uint32_t o4 = (uint32_t)(f2 >> 32) | ((uint32_t)f3 << 16);
-    const uint32_t o5 = (uint32_t)(f3 >> 16);
-    const int64_t tile = (row / 128) * (K / 128) + j / 4;
-    const int sl = (int)(j % 4);
-    const int64_t byte = tile * 12288 + (sl & 1) * 6144 + (row % 128) * 48 + (sl >> 1) * 24;
-    uint2* o = out + byte / 8;
-    o[0] = make_uint2(o0, o1);
-    o[1] = make_uint2(o2, o3);
-    o[2] = make_uint2(o4, o5);
-  }
-  if (scales) {
-    for (int64_t i = first; i < ngroups * prow; i += stride) {
-      const int64_t gi = i / prow, row = i % prow;
-      out_scales[i] = row < rows ? scales[row * ngroups + gi] : S(0);
-    }
+    o[0] = (uint32_t)f0;
+    o[1] = (uint32_t)(f0 >> 32) | ((uint32_t)f1 << 16);
+    o[2] = (uint32_t)(f1 >> 16);
+    o[3] = (uint32_t)f2;
+    o[4] = (uint32_t)(f2 >> 32) | ((uint32_t)f3 << 16);
+    o[5] = (uint32_t)(f3 >> 16);
+  };
+  uint32_t a[6], b[6];
+  fields(x0, a);
+  fields(x1, b);
+  uint4* dst = reinterpret_cast<uint4*>(out + (p * nkb + kb) * 12288 + h * 6144 + r * 48);
+  dst[0] = make_uint4(a[0], a[1], a[2], a[3]);
+  dst[1] = make_uint4(a[4], a[5], b[0], b[1]);
+  dst[2] = make_uint4(b[2], b[3], b[4], b[5]);
+  // the tile that holds a group's first codes writes that group's 128
+  // transposed scales of the panel: out_scales[g][p * 128 + r]
+  if (scales && t < 128 && (kb * 128) % group == 0) {
+    const int64_t g = kb * 128 / group, ngroups = K / group;
+    const int64_t prow = (int64_t)gridDim.y * 128;
+    out_scales[g * prow + row] = row < rows ? scales[row * ngroups + g] : S(0);
   }
 }
 
 hipError_t launch_int4_to_fp6(const uint8_t* codes, const void* scales, bool scale_f16, int64_t rows, int64_t K,
                               int group, uint8_t* out, void* out_scales, hipStream_t s) {
-  const int64_t slots = (rows + 127) / 128 * 128 * (K / 32);
-  int64_t blocks = (slots + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
-  const int64_t ngroups = scales ? K / group : 0;
+  const dim3 grid((unsigned)(K / 128), (unsigned)((rows + 127) / 128));
+  const int g = scales ? group : 128;   // unused without scales
   if (!scales || scale_f16)
-    hipLaunchKernelGGL(int4_to_fp6_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(codes), rows, K, reinterpret_cast<uint2*>(out),
-                       static_cast<const uint16_t*>(scales), ngroups, static_cast<uint16_t*>(out_scales));
+    hipLaunchKernelGGL(int4_to_fp6_kernel<uint16_t>, grid, dim3(256), 0, s, codes, rows, K, out,
+                       static_cast<const uint16_t*>(scales), g, static_cast<uint16_t*>(out_scales));
   else
-    hipLaunchKernelGGL(int4_to_fp6_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       reinterpret_cast<const uint4*>(codes), rows, K, reinterpret_cast<uint2*>(out),
-                       static_cast<const uint32_t*>(scales), ngroups, static_cast<uint32_t*>(out_scales));
+    hipLaunchKernelGGL(int4_to_fp6_kernel<uint32_t>, grid, dim3(256), 0, s, codes, rows, K, out,
+                       static_cast<const uint32_t*>(scales), g, static_cast<uint32_t*>(out_scales));
   return hipGetLastError();
 }
 

@@ -404,7 +404,7 @@ int32_t hr_w8a8_gemm(const int8_t* a_codes, const void* a_scales,
  *   out_scales  [K/G][P] of scale_dtype: scales transposed, zeros for the
  *               padding rows; NULL exactly when scales is.
  *   K           a multiple of 128; group G in {128, 256} dividing K (only read
- *               with scales).
+ *               with scales); rows <= 128 * 65535.
  * All pointers 16-byte aligned.
  */
 int32_t hr_w4a4_to_fp6(const uint8_t* codes, const void* scales, int32_t scale_dtype, int64_t rows, int64_t K,
