@@ -97,12 +97,14 @@ def _gemm_case(M, N, K, G, seed, scale_mode, all_nibbles=False):
 
 
 @pytest.mark.parametrize("G", [128, 256])
-@pytest.mark.parametrize("M", [1, 130, 256])
+@pytest.mark.parametrize("M", [1, 130, 256, 300])
 @pytest.mark.parametrize("scale_mode", ["f16", "f32"])
 def test_gemm_fp6_parity(G, M, scale_mode):
+    """Several 128-row panels with a ragged last one (M = 130, 300), one
+    panel (M = 1), whole panels (M = 256)."""
     hr = _hr()
     N, K = 256, 1024
-    a, w, sa, sw = _gemm_case(M, N, K, G, 800 + M + G, scale_mode, all_nibbles=(M == 130))
+    a, w, sa, sw = _gemm_case(M, N, K, G, 800 + M + G, scale_mode, all_nibbles=(M in (130, 300)))
     (a6, st_a), (w6, st_w) = hr.w4a4_to_fp6(_t(a), _t(sa), G), hr.w4a4_to_fp6(_t(w), _t(sw), G)
     c, acc = hr.w4a4_gemm_fp6(a6, st_a, w6, st_w, G, M, group_acc=True)
     c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(a, sa, w, sw, G, return_sums=True)
