@@ -23,7 +23,7 @@ from . import srchash
 __all__ = ["HRError", "rotate", "rotate_quant_int4", "rotate_quant_int8", "quant_int4", "quant_int8",
            "butterfly_coeffs", "butterfly_apply", "harp_blocks", "harp_apply", "harp_n_params",
            "dequant_int4", "w4a4_gemm", "w4a8_gemm", "w8a8_gemm", "rotate_quant_w4a4_gemm",
-           "fp6_rows", "w4a4_to_fp6", "w4a4_gemm_fp6",
+           "fp6_rows", "w4a4_to_fp6", "rotate_quant_fp6", "w4a4_gemm_fp6",
            "lib", "LIB_PATH", "SYMBOLS",
            "HR_OK", "HR_EINVAL", "HR_EUNSUPPORTED", "HR_EDEVICE", "HR_F32", "HR_BF16", "HR_F16"]
 
@@ -56,6 +56,7 @@ SYMBOLS = {
     "hr_rotate_quant_w4a4_gemm": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _i32, _i64, _i64, _i64, _vp,
                                          _vp, _vp, _vp]),
     "hr_w4a4_to_fp6": (_i32, [_vp, _vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "hr_rotate_quant_fp6": (_i32, [_vp, _i32, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "hr_w4a4_gemm_fp6": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
 }
 
@@ -546,6 +547,30 @@ def w4a4_to_fp6(codes: torch.Tensor, scales: torch.Tensor | None = None, group: 
     pc, ps, po, pos = _ptrs(ac, asc, ("out", o), ("out_scales", os_))
     _check(lib.hr_w4a4_to_fp6(pc, ps, _dtype_code(sd), rows, K, group, po, pos, _stream(codes.device)),
            "hr_w4a4_to_fp6")
+    return o, os_
+
+
+def rotate_quant_fp6(x: torch.Tensor, group: int, signs: torch.Tensor | None = None,
+                     scale_dtype=torch.float16, out: torch.Tensor | None = None,
+                     out_scales: torch.Tensor | None = None):
+    """Rotation + int4 quantization of bf16 rows (n = 2048 or 4096) with the
+    codes in the tiled fp6 format and the scales transposed
+    (hr_rotate_quant_fp6): returns (tiles [fp6_rows(rows)][n*3/4] uint8,
+    scales [n/G][fp6_rows(rows)]); the padding rows are not written."""
+    rows, n = _rows_of(x, "x", (torch.bfloat16,))
+    ax = _arg(x, "x", torch.bfloat16, (rows, n))
+    asg = _arg(signs, "signs", torch.int8, (n,))
+    if group not in (128, 256) or n not in (2048, 4096):
+        raise ValueError(f"group={group} must be 128 or 256 and n={n} 2048 or 4096")
+    sd = _scale_dtype(scale_dtype)
+    P = fp6_rows(rows)
+    _arg(out, "out", torch.uint8, (P, n * 3 // 4))
+    _arg(out_scales, "out_scales", sd, (n // group, P))
+    o = out if out is not None else torch.empty((P, n * 3 // 4), dtype=torch.uint8, device=x.device)
+    os_ = out_scales if out_scales is not None else torch.empty((n // group, P), dtype=sd, device=x.device)
+    px, ps, po, pos = _ptrs(ax, asg, ("out", o), ("out_scales", os_))
+    _check(lib.hr_rotate_quant_fp6(px, HR_BF16, ps, rows, n, group, _dtype_code(sd), po, pos, _stream(x.device)),
+           "hr_rotate_quant_fp6")
     return o, os_
 
 

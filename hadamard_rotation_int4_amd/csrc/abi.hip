@@ -487,6 +487,39 @@ int32_t hr_w4a4_to_fp6(const uint8_t* codes, const void* scales, int32_t scale_d
                   fn);
 }
 
+int32_t hr_rotate_quant_fp6(const void* x, int32_t x_dtype, const int8_t* signs, int64_t rows, int32_t n,
+                            int32_t group, int32_t scale_dtype, uint8_t* tiles, void* scales, void* stream) {
+  const char* fn = "hr_rotate_quant_fp6";
+  if (rows < 0) return fail(HR_EINVAL, "%s: rows < 0", fn);
+  if (rows > 0 && (!x || !tiles || !scales)) return fail(HR_EINVAL, "%s: x, tiles and scales are required", fn);
+  if (x_dtype != HR_BF16) return fail(HR_EUNSUPPORTED, "%s: x_dtype must be HR_BF16", fn);
+  if (!aligned16(x) || !aligned16(tiles) || !aligned16(scales))
+    return fail(HR_EINVAL, "%s: x, tiles and scales must be 16-byte aligned", fn);
+  if (scale_dtype != HR_F16 && scale_dtype != HR_F32)
+    return fail(HR_EINVAL, "%s: scale_dtype must be HR_F16 or HR_F32", fn);
+  if (n != 2048 && n != 4096) return fail(HR_EUNSUPPORTED, "%s: n=%d not 2048 or 4096", fn, n);
+  if (group != 128 && group != 256) return fail(HR_EUNSUPPORTED, "%s: group=%d not in {128,256}", fn, group);
+  if (rows == 0) return ok();
+  hr::RhtArgs a{};
+  a.x = x;
+  a.x_bf16 = 1;
+  a.rows = rows;
+  a.n = n;
+  a.m = 1;
+  a.p = n;
+  a.signs = signs;
+  a.block = nullptr;
+  a.y = nullptr;
+  a.group = group;
+  a.codes = tiles;
+  a.bits = 6;
+  a.scales = scales;
+  a.scale_f16 = scale_dtype == HR_F16;
+  if (!hr::launch_rotate_quant_fp6(a, static_cast<hipStream_t>(stream)))
+    return fail(HR_EUNSUPPORTED, "%s: unsupported case", fn);
+  return from_hip(hipGetLastError(), fn);
+}
+
 int32_t hr_w4a4_gemm_fp6(const uint8_t* a_f6, const void* a_scales, const uint8_t* w_f6, const void* w_scales,
                          int32_t scale_dtype, int64_t M, int64_t N, int64_t K, int32_t group, float* c,
                          int32_t* group_acc, void* stream) {

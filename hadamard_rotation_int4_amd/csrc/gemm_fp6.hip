@@ -30,6 +30,7 @@
 // that go with a tiled operand are transposed, [K / G][padded rows], zeros for
 // the padding rows.
 #include "hr_internal.h"
+#include "hr_device.h"
 
 namespace hr {
 
@@ -40,20 +41,8 @@ typedef int f6_v2i __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- conversion
 
-// nibbles 0..3 of t moved to bits 0, 6, 12, 18
-__device__ __forceinline__ uint32_t f6_spread4(uint32_t t) {
-  const uint32_t u = (t & 0x00FFu) | ((t & 0xFF00u) << 4);   // nibbles at 0, 4, 12, 16
-  return (u & 0x0F00Fu) | ((u & 0xF00F0u) << 2);              // nibbles at 0, 6, 12, 18
-}
-
-// 8 two's-complement nibbles (code 8 d + e in bits 4 e) -> 8 fp6 fields (48 bits)
-__device__ __forceinline__ uint64_t f6_fields8(uint32_t x) {
-  const uint32_t s = (x >> 3) & 0x11111111u;                 // sign of each nibble at its bit 0
-  const uint32_t m = (x ^ (s * 15u)) + s;                     // |code| per nibble (0..8), no carries
-  const uint32_t lo = f6_spread4(m & 0xFFFFu) | (f6_spread4(s & 0xFFFFu) << 5);
-  const uint32_t hi = f6_spread4(m >> 16) | (f6_spread4(s >> 16) << 5);
-  return (uint64_t)lo | ((uint64_t)hi << 24);
-}
+// (f6_fields8, which turns 8 packed int4 codes into 8 fp6 fields, is in
+// hr_device.h: the fp6-output rotation kernel uses it too)
 
 // One workgroup of 256 threads per output tile (panel p = blockIdx.y, block
 // kb = blockIdx.x): thread t writes row r = t % 128 of plane h = t / 128, the

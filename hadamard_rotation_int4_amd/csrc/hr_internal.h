@@ -17,8 +17,8 @@ struct RhtArgs {
   const float* block;    // [m][m], null when m == 1
   float* y;              // fp32 output or null
   int group;             // quantization group (when codes != null)
-  uint8_t* codes;        // packed int4 (bits 4) or int8 (bits 8) codes, or null
-  int bits;              // 4 or 8 (when codes != null)
+  uint8_t* codes;        // packed int4 (bits 4), int8 (bits 8) or tiled fp6 (bits 6) codes, or null
+  int bits;              // 4, 8 or 6 (when codes != null)
   void* scales;          // scale output or null
   int scale_f16;         // 1: fp16 scales, 0: fp32 scales
 };
@@ -126,6 +126,9 @@ bool launch_butterfly4096(const ButterflyArgs& a, hipStream_t s);  // false: not
 hipError_t launch_dequant(const uint8_t* codes, const void* scales, int scale_f16, int64_t rows,
                           int n, int group, float* out, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// bf16 rows of n = 2048 or 4096, int4 codes in the tiled fp6 format (a.codes)
+// and transposed scales (a.scales), G = 128 or 256; false for other cases
+bool launch_rotate_quant_fp6(const RhtArgs& a, hipStream_t s);
 // scales may be null (then out_scales, scale_f16 and group are unused)
 hipError_t launch_int4_to_fp6(const uint8_t* codes, const void* scales, bool scale_f16, int64_t rows, int64_t K,
                               int group, uint8_t* out, void* out_scales, hipStream_t s);

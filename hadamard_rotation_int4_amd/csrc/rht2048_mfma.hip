@@ -24,6 +24,21 @@
 //   Codes: a lane owns four runs of 8 consecutive outputs; they are staged
 //     through LDS (swizzled, conflict-free) and written as contiguous 1 KB
 //     runs, one per store instruction (one per int4 row, two per int8 row).
+//   fp6 output (BITS = 6): the int4 codes as fp6 e2m3 fields in the tiled
+//     operand format of the fp6 GEMM (panels of 128 rows, 12288-byte tiles of
+//     128 codes, two planes each holding slots h and h + 2 of a row at row *
+//     48), and the scales transposed to [n / G][padded rows].  A row holds
+//     only 48 contiguous bytes per plane of a tile, so a wave takes its rows
+//     in groups of 4 consecutive ones (a workgroup 16) and stages a group's
+//     codes in LDS in the tiles' byte order: per chunk, 32 regions (block,
+//     plane) of 4 x 48 = 192 contiguous bytes, which go out as 16-byte
+//     stores covering whole 64-byte sectors.  A run of 8 codes (slot m,
+//     offset 8 g) is 6 bytes at byte 24 (m >> 1) + 6 g of its row in region
+//     (block, m & 1).  The two regions of a block sit 400 bytes apart from
+//     the next block's in LDS (384 would put the 16 blocks a staging store
+//     touches in the same banks).  The fields come from the fp32 -> fp6
+//     pack conversion of the exact integer codes with scale 8 (code / 8 is
+//     an e2m3 value), 32 codes per instruction.
 #include "mfma2048.h"
 
 namespace hr {
@@ -52,8 +67,20 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
   constexpr int N = CH * P;        // row
   const int lane = threadIdx.x & 63;
   const int wib = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wib;
+  // fp6 output: workgroups are dealt to the 8 XCDs in turn, so block b
+  // takes place (b % 8) (blocks / 8) + b / 8: each XCD then covers runs of
+  // consecutive rows, and the lines of a tile or of the transposed scales
+  // are written from one L2
+  int64_t bid = blockIdx.x;
+  if (BITS == 6 && (gridDim.x & 7) == 0) bid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int64_t wave = bid * (blockDim.x >> 6) + wib;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  // the k-th row of this wave: rows wave + k nwaves, or for fp6 output groups
+  // of 4 consecutive rows (group wave + (k / 4) nwaves)
+  auto row_at = [&](int k) -> int64_t {
+    if (BITS == 6) return 4 * (wave + (int64_t)(k >> 2) * nwaves) + (k & 3);
+    return wave + (int64_t)k * nwaves;
+  };
   Mfma2048 M[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) mfma2048_init(M[c], lane, signs ? signs + c * P : nullptr);
@@ -61,9 +88,12 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
   const float tau = M[0].tau;
 
   // LDS of this wave: two row stages (256 slots of 16 bytes per chunk) and
-  // one chunk of codes
+  // one chunk of codes (fp6: the codes of a group of 4 rows, every chunk)
   __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][2][CH * 256];
-  __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][BITS == 8 ? 128 : 64];
+  __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][BITS == 8 ? 128 : BITS == 6 ? CH * 400 : 64];
+  // fp6: the group's scales, [group][row of the group] (fp16 or fp32 bits)
+  constexpr int SES = SCALE_F16 ? 2 : 4;
+  __shared__ __attribute__((aligned(16))) uint8_t scale_lds[4][BITS == 6 ? 4 * (N / G) * SES : 16];
   // fp32 output: this wave's 8 KB output row, staged so it leaves as 1 KB stores
   __shared__ __attribute__((aligned(16))) f32x4 out_lds[OUT_F32 ? 4 : 1][OUT_F32 ? 512 : 1];
   // element offset of this lane's piece within a row, per load j: + 32 j
@@ -92,8 +122,9 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
     switch (younger) {
 #define HR_VMW(V) \
       case V: __builtin_amdgcn_s_waitcnt(((V) & 15) | (((V) >> 4) << 14) | 0x0F70); break;
-      HR_VMW(0) HR_VMW(2) HR_VMW(3) HR_VMW(4) HR_VMW(6) HR_VMW(7) HR_VMW(8) HR_VMW(10)
-      HR_VMW(12) HR_VMW(14) HR_VMW(16) HR_VMW(20) HR_VMW(24) HR_VMW(32) HR_VMW(40)
+      HR_VMW(0) HR_VMW(1) HR_VMW(2) HR_VMW(3) HR_VMW(4) HR_VMW(5) HR_VMW(6) HR_VMW(7) HR_VMW(8)
+      HR_VMW(10) HR_VMW(11) HR_VMW(12) HR_VMW(13) HR_VMW(14) HR_VMW(16) HR_VMW(20) HR_VMW(21)
+      HR_VMW(24) HR_VMW(32) HR_VMW(40)
 #undef HR_VMW
       default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // vmcnt(0)
     }
@@ -230,7 +261,18 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
       else if (G == 64) si = g < 2 ? s0 + 2 * a4 + g : -1;
       else if (G == 128) si = g == 0 ? s0 + a4 : -1;
       else si = (g == 0 && (a4 & 1) == 0) ? s0 + (a4 >> 1) : -1;
-      if (si >= 0) {
+      if (BITS == 6) {
+        // staged for flush6 (transposed there), in asm like the codes
+        if (si >= 0) {
+          const uint32_t a = (uint32_t)(uintptr_t)&scale_lds[wib][0] +
+                             (uint32_t)(4 * (si - row * (N / G)) + (row & 3)) * SES;
+          if (SCALE_F16)
+            asm volatile("ds_write_b16 %0, %1" : : "v"(a), "v"((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s_own))
+                         : "memory");
+          else
+            asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(__float_as_uint(s_own)) : "memory");
+        }
+      } else if (si >= 0) {
         if (SCALE_F16) reinterpret_cast<_Float16*>(scales)[si] = (_Float16)s_own;
         else reinterpret_cast<float*>(scales)[si] = s_own;
       }
@@ -239,8 +281,11 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
     const bool tiny = !SCALE_F16 && __builtin_amdgcn_ballot_w64(need_up) != 0;
     // q + M rounds y k to an integer in the low mantissa bits (ties to even)
     constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
-    const float M = BITS == 8 ? 12582912.0f : 12582920.0f;   // 1.5 * 2^23 (+ 8 for nibbles)
+    const float M = BITS == 4 ? 12582920.0f : 12582912.0f;   // 1.5 * 2^23 (+ 8 for nibbles)
     u32x4* cl = &code_lds[wib][0];
+    // fp6: the codes as floats, in the conversion's operand order (field 2 i
+    // from qa[i], 2 i + 1 from qb[i]): run m, element e at field 8 m + e
+    float qa[BITS == 6 ? 16 : 1], qb[BITS == 6 ? 16 : 1];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int gl = G == 32 ? m : G == 64 ? (m >> 1) : 0;
@@ -259,6 +304,12 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
       if (BITS == 4) {
         // dword 16 a + 4 m + g of the row: 16-byte block (a, m) at 4 a + (m ^ (a >> 2 & 3))
         reinterpret_cast<uint32_t*>(cl)[4 * (4 * a4 + (m ^ ((a4 >> 2) & 3))) + g] = pack8(rr);
+      } else if (BITS == 6) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qa[4 * m + i] = rr[2 * i] - M;        // exact
+          qb[4 * m + i] = rr[2 * i + 1] - M;
+        }
       } else {
         // the low byte of each float is its two's-complement code
         uint32_t u[8];
@@ -273,12 +324,39 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
         reinterpret_cast<uint2*>(cl)[16 * a4 + ((4 * m + g) ^ (2 * (a4 >> 1)))] = make_uint2(d0, d1);
       }
     }
-    if (BITS == 4) {
+    if (BITS == 6) {
+      typedef float f32x16 __attribute__((ext_vector_type(16)));
+      typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+      f32x16 va, vb;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        va[i] = qa[i];
+        vb[i] = qb[i];
+      }
+      // 32 fields of 6 bits: run m at bits 48 m .. 48 m + 47
+      const u32x6 d = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(va, vb, 8.0f);
+      // run m goes to byte 192 (m & 1) + 24 (m >> 1) of the lane's base, as
+      // three 16-bit pieces (in asm: compiler-visible stores here were given
+      // a wait for the row stages' pending loads, a different array)
+      const uint32_t la =
+          (uint32_t)(uintptr_t)cl + 6400 * ch + 400 * a4 + 48 * (int)(row & 3) + 6 * g;
+      asm volatile(
+          "ds_write_b16 %0, %1\n\tds_write_b16_d16_hi %0, %1 offset:2\n\tds_write_b16 %0, %2 offset:4\n\t"
+          "ds_write_b16_d16_hi %0, %2 offset:192\n\tds_write_b16 %0, %3 offset:194\n\t"
+          "ds_write_b16_d16_hi %0, %3 offset:196\n\t"
+          "ds_write_b16 %0, %4 offset:24\n\tds_write_b16_d16_hi %0, %4 offset:26\n\tds_write_b16 %0, %5 offset:28\n\t"
+          "ds_write_b16_d16_hi %0, %5 offset:216\n\tds_write_b16 %0, %6 offset:218\n\t"
+          "ds_write_b16_d16_hi %0, %6 offset:220"
+          :
+          : "v"(la), "v"(d[0]), "v"(d[1]), "v"(d[2]), "v"(d[3]), "v"(d[4]), "v"(d[5])
+          : "memory");
+      // stored by flush6 once the group's rows are staged
+    } else if (BITS == 4) {
       // lane i stores bytes 16 i .. 16 i + 15 of the row: block (i >> 2, i & 3)
       const int ra = lane >> 2, rm = lane & 3;
       const u32x4 out = cl[4 * ra + (rm ^ ((ra >> 2) & 3))];
       __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + row * (N / 2) + ch * (P / 2)) + lane);
-    } else {
+    } else if (BITS == 8) {
       // 16-byte block b = 8 a + k of the row sits at 8 a + (k ^ (a >> 1))
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -309,30 +387,92 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
     emit(row, 1, dif);
   };
 
-  // Vector-memory operations per processed row (every wave issues each of
-  // them: the scale-storing lanes are in every wave): one code store per
-  // chunk (two for int8) and one scale store, or eight fp32 stores per chunk
-  constexpr int SPR = CH * (OUT_F32 ? 8 : (BITS == 8 ? 2 : 1) + 1);
+  // fp6: the staged group of rows r0 .. r0 + 3 (those below rows) to the
+  // tiles; lane i of store t takes 16-byte piece 64 t + i of a chunk's image,
+  // region p / 12, row (p % 12) / 3.  Then lane i < n / G stores group i's
+  // scales of the 4 rows (contiguous in the transposed scale array).
+  auto flush6 = [&](int64_t r0) {
+    const int64_t valid = rows - r0;
+    const int64_t prow = (rows + 127) / 128 * 128;
+    if (lane < N / G) {
+      const uint8_t* src = &scale_lds[wib][4 * SES * lane];
+      uint8_t* dst = static_cast<uint8_t*>(scales) + (lane * prow + r0) * SES;
+      if (valid >= 4) {
+        if (SCALE_F16) *reinterpret_cast<uint64_t*>(dst) = *reinterpret_cast<const uint64_t*>(src);
+        else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          if (j >= valid) break;
+          if (SCALE_F16) reinterpret_cast<uint16_t*>(dst)[j] = reinterpret_cast<const uint16_t*>(src)[j];
+          else reinterpret_cast<uint32_t*>(dst)[j] = reinterpret_cast<const uint32_t*>(src)[j];
+        }
+      }
+    }
+    // LDS address and tile offset of each of the lane's 6 pieces per chunk
+    const uint32_t lb = (uint32_t)(uintptr_t)&code_lds[wib][0];
+    uint32_t la[6];
+    int32_t go[6];
+    bool ok[6];
+#pragma unroll
+    for (int t = 0; t < 6; ++t) {
+      const int p = 64 * t + lane, region = p / 12, in = p % 12;
+      la[t] = lb + 16 * (25 * (region >> 1) + 12 * (region & 1) + in);
+      go[t] = (region >> 1) * 12288 + (region & 1) * 6144 + 16 * in;
+      ok[t] = in / 3 < valid;
+    }
+    uint8_t* const gb = codes + (r0 >> 7) * (N / 128) * 12288 + (r0 & 127) * 48;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // (reads in asm: compiler-visible ones were given a wait for every
+      // outstanding memory operation)
+      u32x4 v[6];
+      asm volatile(
+          "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\t"
+          "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\ts_waitcnt lgkmcnt(0)"
+          : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5])
+          : "v"(la[0] + 6400 * c), "v"(la[1] + 6400 * c), "v"(la[2] + 6400 * c), "v"(la[3] + 6400 * c),
+            "v"(la[4] + 6400 * c), "v"(la[5] + 6400 * c)
+          : "memory");
+#pragma unroll
+      for (int t = 0; t < 6; ++t)
+        if (ok[t]) __builtin_nontemporal_store(v[t], reinterpret_cast<u32x4*>(gb + c * (P / 128) * 12288 + go[t]));
+    }
+  };
+
+  // Vector-memory operations issued while processing the k-th row (every
+  // wave issues each of them: the scale-storing lanes are in every wave):
+  // per chunk one scale store and one code store (two for int8), or eight
+  // fp32 stores; for fp6 six per chunk and one scale store after the fourth
+  // row of a group, none otherwise
+  auto stores_at = [&](int k) -> int {
+    if (OUT_F32) return 8 * CH;
+    if (BITS == 6) return (k & 3) == 3 ? 6 * CH + 1 : 0;
+    return CH * (BITS == 8 ? 3 : 2);
+  };
   constexpr int LPR = 4 * CH;      // loads per row
-  int64_t row = wave;
+  int64_t row = row_at(0);
   if (row < rows) issue(row, 0);
-  if (row + nwaves < rows) issue(row + nwaves, 1);
-  for (int st = 0, it = 0; row < rows; row += nwaves, st ^= 1, ++it) {
+  if (row_at(1) < rows) issue(row_at(1), 1);
+  for (int st = 0, k = 0; row < rows; ++k, row = row_at(k), st ^= 1) {
     u32x4 b[CH][4];
     // issued after this row's loads: the next row's loads (if any; issued
     // before this row's loads only in the prologue), and the stores of the
-    // rows processed since this row's loads were issued (none, one, then two)
-    const bool next = row + nwaves < rows;
-    const int younger = (next ? LPR : 0) + (it == 0 ? 0 : it == 1 ? SPR : 2 * SPR);
+    // rows processed since this row's loads were issued (none, one, then two;
+    // a group's last fp6 flush is never followed by a wait)
+    const bool next = row_at(k + 1) < rows;
+    const int younger = (next ? LPR : 0) + (k >= 1 ? stores_at(k - 1) : 0) + (k >= 2 ? stores_at(k - 2) : 0);
     read_stage(st, younger, b);
-    if (row + 2 * nwaves < rows) issue(row + 2 * nwaves, st);
+    if (row_at(k + 2) < rows) issue(row_at(k + 2), st);
     process(row, b);
+    if (BITS == 6 && ((row & 3) == 3 || row + 1 == rows)) flush6(row & ~(int64_t)3);
   }
 }
 
 template <int G, bool SCALE_F16, bool OUT_F32, int BITS = 4>
 static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
-  int64_t blocks = (a.rows + 3) / 4;              // 4 waves per block, one row per wave
+  // 4 waves per block, one row per wave (fp6: a group of 4 rows per wave)
+  int64_t blocks = BITS == 6 ? (a.rows + 15) / 16 : (a.rows + 3) / 4;
   const int64_t cap = 256 * (a.p == 4096 ? mfma_blocks_per_cu<OUT_F32, 2>() : mfma_blocks_per_cu<OUT_F32, 1>());
   if (blocks > cap) blocks = cap;
   if (a.p == 4096)
@@ -343,6 +483,24 @@ static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
     hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS>), dim3((unsigned)blocks),
                        dim3(256), 0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
                        a.scales, norm);
+}
+
+// bf16 rows of n = 2048 or 4096: fused int4 quantization with the codes in
+// the tiled fp6 format and the scales transposed (G = 128 or 256), any row
+// count.  Returns false for other cases.
+bool launch_rotate_quant_fp6(const RhtArgs& a, hipStream_t s) {
+  if (!a.x_bf16 || (a.p != 2048 && a.p != 4096) || a.m != 1 || !a.codes || a.y) return false;
+  const float norm = (float)(1.0 / sqrt((double)a.p));
+  if (a.group == 128) {
+    if (a.scale_f16) launch_mfma<128, true, false, 6>(a, norm, s);
+    else launch_mfma<128, false, false, 6>(a, norm, s);
+  } else if (a.group == 256) {
+    if (a.scale_f16) launch_mfma<256, true, false, 6>(a, norm, s);
+    else launch_mfma<256, false, false, 6>(a, norm, s);
+  } else {
+    return false;
+  }
+  return true;
 }
 
 // bf16 rows of n = 2048 or 4096 (m = 1): fp32 output or fused int4 / int8

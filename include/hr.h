@@ -54,7 +54,7 @@ typedef enum {
 } hr_dtype;
 
 /* ABI version of this header (bumped on any signature change). */
-#define HR_ABI_VERSION 4
+#define HR_ABI_VERSION 5
 int32_t hr_abi_version(void);
 
 /* Identifier of the sources the library was built from (a hash of every
@@ -411,6 +411,28 @@ int32_t hr_w4a4_to_fp6(const uint8_t* codes, const void* scales, int32_t scale_d
                        int32_t group, uint8_t* out, void* out_scales, void* stream);
 
 /*
+ * hr_rotate_quant_fp6 -- hr_rotate_quant_int4 (m = 1) with its codes written
+ * straight into the tiled fp6 format of hr_w4a4_to_fp6 and its scales
+ * transposed, for activations headed to hr_w4a4_gemm_fp6.
+ *
+ * Defines: as hr_rotate_quant_int4 ("Experiment -- Hadamard rotation for int4
+ * (W4A4) accuracy", Hypothesis and Method), the same codes and scales.
+ *
+ *   x        [rows][n] bf16 (x_dtype must be HR_BF16); n = 2048 or 4096.
+ *   signs    [n] int8 +-1 or NULL.
+ *   group    G in {128, 256}.
+ *   tiles    P * n * 3 / 4 bytes, P = ceil(rows / 128) * 128, as
+ *            hr_w4a4_to_fp6 writes them, except that the padding rows of the
+ *            last panel are not written (hr_w4a4_gemm_fp6 stores no output
+ *            from them, so their contents do not matter).
+ *   scales   [n / G][P] of scale_dtype (HR_F16 or HR_F32), transposed; the
+ *            padding rows' entries are not written either.
+ * All pointers 16-byte aligned.
+ */
+int32_t hr_rotate_quant_fp6(const void* x, int32_t x_dtype, const int8_t* signs, int64_t rows, int32_t n,
+                            int32_t group, int32_t scale_dtype, uint8_t* tiles, void* scales, void* stream);
+
+/*
  * hr_w4a4_gemm_fp6 -- the W4A4 GEMM of hr_w4a4_gemm on operands in the tiled
  * fp6 format of hr_w4a4_to_fp6, on v_mfma_f32_32x32x64_f8f6f4.
  *
@@ -420,7 +442,8 @@ int32_t hr_w4a4_to_fp6(const uint8_t* codes, const void* scales, int32_t scale_d
  * acc[m][n][g] is the exact integer group sum and C matches hr_w4a4_gemm.
  *
  *   a_f6, a_scales  activation codes of M rows and their transposed scales,
- *                   as hr_w4a4_to_fp6 writes them (ceil(M / 128) panels).
+ *                   as hr_w4a4_to_fp6 or hr_rotate_quant_fp6 write them
+ *                   (ceil(M / 128) panels; padding rows may hold anything).
  *   w_f6, w_scales  weight codes of N rows and scales, the same way.
  *   scale_dtype, c, group_acc: as hr_w4a4_gemm.
  *   M >= 0; N a multiple of 128; K a multiple of G, K <= 65536.

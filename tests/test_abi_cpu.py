@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert hr.lib.hr_abi_version() == 4
+    assert hr.lib.hr_abi_version() == 5
     for st in (hr.HR_OK, hr.HR_EINVAL, hr.HR_EUNSUPPORTED, hr.HR_EDEVICE):
         assert hr.lib.hr_status_string(st).startswith(b"HR_")
     assert b"unknown" in hr.lib.hr_status_string(99)
@@ -171,6 +171,16 @@ def test_fp6_validation():
     assert gemm(P, P, P, P, hr.HR_F16, 16, 128, 384, 256, P, None, None) == hr.HR_EUNSUPPORTED  # K % G
     assert gemm(P, P, P, P, hr.HR_F16, 16, 128, 131072, 128, P, None, None) == hr.HR_EUNSUPPORTED
     assert gemm(P, P, P, P, hr.HR_F16, 0, 128, 384, 128, P, None, None) == hr.HR_OK
+    rq = hr.lib.hr_rotate_quant_fp6
+    # x, x_dtype, signs, rows, n, group, sdt, tiles, scales, stream
+    assert rq(None, hr.HR_BF16, None, 4, 2048, 128, hr.HR_F16, P, P, None) == hr.HR_EINVAL
+    assert rq(P, hr.HR_F32, None, 4, 2048, 128, hr.HR_F16, P, P, None) == hr.HR_EUNSUPPORTED
+    assert rq(P, hr.HR_BF16, None, 4, 1024, 128, hr.HR_F16, P, P, None) == hr.HR_EUNSUPPORTED
+    assert rq(P, hr.HR_BF16, None, 4, 2048, 64, hr.HR_F16, P, P, None) == hr.HR_EUNSUPPORTED
+    assert rq(P, hr.HR_BF16, None, 4, 2048, 128, hr.HR_BF16, P, P, None) == hr.HR_EINVAL
+    assert rq(P, hr.HR_BF16, None, 4, 2048, 128, hr.HR_F16, P + 4, P, None) == hr.HR_EINVAL
+    assert rq(P, hr.HR_BF16, None, -1, 2048, 128, hr.HR_F16, P, P, None) == hr.HR_EINVAL
+    assert rq(P, hr.HR_BF16, None, 0, 4096, 256, hr.HR_F32, P, P, None) == hr.HR_OK
 
 
 def _rad(*b):

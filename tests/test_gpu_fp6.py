@@ -11,7 +11,7 @@ import torch
 
 import hr_inputs
 import oracle
-from parity import check_gemm
+from parity import check_gemm, check_quant
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +45,22 @@ def decode_fp6_tiles(f6: np.ndarray, rows: int) -> np.ndarray:
                 assert f & 0x10 == 0 and (f & 0x0F) <= 8, (r, j, e, f)
                 out[r, 32 * j + e] = -(f & 0x0F) if f & 0x20 else (f & 0x0F)
     return out
+
+
+def decode_fp6_tiles_np(f6: np.ndarray, rows: int) -> np.ndarray:
+    """The same decoding as decode_fp6_tiles, vectorised with numpy (for the
+    larger cases): [padded rows][K*3/4] bytes -> int codes [rows][K]; only
+    the first rows are checked and returned (padding rows may hold anything)."""
+    prow, nb = f6.shape
+    K = nb * 4 // 3
+    P, KB = prow // 128, K // 128
+    t = f6.reshape(P, KB, 2, 128, 2, 24)              # panel, block, plane h, row, slot pair, 24 bytes
+    bits = np.unpackbits(t, axis=-1, bitorder="little").reshape(P, KB, 2, 128, 2, 32, 6)
+    f = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)      # [P][KB][h][r][pair][e]
+    # slot j of a block = plane j & 1, pair j >> 1
+    f = f.transpose(0, 3, 1, 4, 2, 5).reshape(P * 128, K)[:rows]  # panel, row, block, pair, plane, e
+    assert not (f & 0x10).any() and ((f & 0x0F) <= 8).all()
+    return np.where(f & 0x20, -(f & 0x0F), f & 0x0F)
 
 
 def _all_nibble_codes(rng, rows, K):
@@ -152,3 +168,49 @@ def test_gemm_fp6_4096_sampled():
     c8 = hr.w4a4_gemm(_t(gi.a_codes), _t(gi.a_scales), _t(gi.w_codes), _t(gi.w_scales), 128)
     diff = (c - c8).abs().max().item()
     assert diff <= 1e-5 * float(np.abs(bound).max()), diff
+
+
+@pytest.mark.parametrize("rows", [1, 130, 300])
+@pytest.mark.parametrize("n", [2048, 4096])
+@pytest.mark.parametrize("G", [128, 256])
+@pytest.mark.parametrize("scale_mode", ["f16", "f32"])
+def test_rotate_quant_fp6(rows, n, G, scale_mode):
+    """hr_rotate_quant_fp6: the tiles hold the oracle's codes of the rotated
+    rows and the transposed scales its scales (the parity rules of the int4
+    path), and they equal the int4 entry's codes and scales bit for bit."""
+    hr = _hr()
+    ri = hr_inputs.rht_inputs(rows=rows, n=n, seed=870 + rows + n + G)
+    x, d = ri.x.to(DEV), _t(ri.signs)
+    sdt = torch.float16 if scale_mode == "f16" else torch.float32
+    tiles, st = hr.rotate_quant_fp6(x, G, d, scale_dtype=sdt)
+    assert tiles.shape == (hr.fp6_rows(rows), n * 3 // 4) and st.shape == (n // G, hr.fp6_rows(rows))
+    q = decode_fp6_tiles_np(tiles.cpu().numpy(), rows)
+    sc = st.cpu().numpy()[:, :rows].T.copy()
+    y64 = oracle.hadamard.rht(ri.x.float().numpy(), ri.signs)
+    check_quant(oracle.quant.pack_int4(q), sc, y64, G, scale_mode)
+    codes4, scales4 = hr.rotate_quant_int4(x, G, d, scale_dtype=sdt)
+    np.testing.assert_array_equal(q, oracle.quant.unpack_int4(codes4.cpu().numpy()))
+    np.testing.assert_array_equal(sc.view(np.uint8), scales4.cpu().numpy().view(np.uint8))
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_rotate_quant_fp6_then_gemm(M):
+    """bf16 activations -> hr_rotate_quant_fp6 -> hr_w4a4_gemm_fp6 against the
+    oracle GEMM on the activation codes the tiles hold and the weight codes
+    (int32 group sums exact); the padding rows were never written."""
+    hr = _hr()
+    N, K, G = 256, 4096, 128
+    ri = hr_inputs.rht_inputs(rows=M, n=K, seed=880 + M)
+    gi = hr_inputs.gemm_inputs(M=1, N=N, K=K, group=G, seed=881)
+    x, d = ri.x.to(DEV), _t(ri.signs)
+    tiles = torch.full((hr.fp6_rows(M), K * 3 // 4), 0xFF, dtype=torch.uint8, device=DEV)
+    st = torch.full((K // G, hr.fp6_rows(M)), float("nan"), dtype=torch.float16, device=DEV)
+    hr.rotate_quant_fp6(x, G, d, out=tiles, out_scales=st)
+    w6, stw = hr.w4a4_to_fp6(_t(gi.w_codes), _t(gi.w_scales), G)
+    c, acc = hr.w4a4_gemm_fp6(tiles, st, w6, stw, G, M, group_acc=True)
+    a_codes = oracle.quant.pack_int4(decode_fp6_tiles_np(tiles.cpu().numpy(), M))
+    a_scales = st.cpu().numpy()[:, :M].T.copy()
+    c_ref, acc_ref, bound = oracle.gemm.w4a4_gemm(a_codes, a_scales, gi.w_codes, gi.w_scales, G,
+                                                  return_sums=True)
+    check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
+    assert torch.isfinite(c).all()
