@@ -338,6 +338,15 @@ def main(argv=None):
         kernels["rht_quant_int8_bf16_65536x2048_g128"] = hbm_entry(
             ms8, ROWS * N * 2 + ROWS * N + ROWS * (N // GROUP) * 2)
         del c8
+        # the codes straight into the tiled fp6 operand format of the fp6 GEMM
+        # (6 bits per code), scales transposed
+        f6 = [torch.empty((ROWS, N * 3 // 4), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        sf6 = [torch.empty((N // GROUP, ROWS), dtype=torch.float16, device=dev) for _ in range(nbuf)]
+        msf6 = _timed(lambda i: hr.rotate_quant_fp6(xs[i], GROUP, d, out=f6[i], out_scales=sf6[i]),
+                      args.steps, args.warmup, nbuf)
+        kernels["rht_quant_fp6_bf16_65536x2048_g128"] = hbm_entry(
+            msf6, ROWS * N * 2 + ROWS * N * 3 // 4 + ROWS * (N // GROUP) * 2)
+        del f6, sf6
         # the same quantization without the rotation (the probe's plain operands)
         msq = _timed(lambda i: hr.quant_int4(xs[i], GROUP, codes=codes[i], scales=scales[i]),
                      args.steps, args.warmup, nbuf)
@@ -426,7 +435,28 @@ def main(argv=None):
         kernels["w4a4_gemm_fp6_with_a_convert_4096x4096x4096_g128"] = gemm_entry(
             ms6c, 4096, b6 + 4096 * 2048 + 4096 * 32 * 2 + 4096 * 3072 + 4096 * 32 * 2, timing="eager launches",
             operands="packed int4 activations converted per call, weights converted once")
-        del ad, sad, cg, a6, sta, w6, stw
+        # the whole activation path from bf16 (rotation + quantization, then
+        # the GEMM): into fp6 tiles + fp6 GEMM, against packed int4 + int8 GEMM
+        ri = hr_inputs.rht_inputs(rows=4096, n=4096)
+        xa, da = ri.x.to(dev), t(ri.signs)
+
+        def rq_fp6_gemm(i):
+            hr.rotate_quant_fp6(xa, 128, da, out=a6, out_scales=sta)
+            hr.w4a4_gemm_fp6(a6, sta, w6, stw, 128, 4096, out=cg)
+
+        def rq_int4_gemm(i):
+            hr.rotate_quant_int4(xa, 128, da, codes=ad, scales=sad)
+            hr.w4a4_gemm(ad, sad, wd, swd, 128, out=cg)
+        ms_rf = _timed(rq_fp6_gemm, args.steps, args.warmup)
+        ms_ri = _timed(rq_int4_gemm, args.steps, args.warmup)
+        xbytes = 4096 * 4096 * 2
+        kernels["rotate_quant_fp6_then_gemm_fp6_4096x4096x4096_g128"] = gemm_entry(
+            ms_rf, 4096, b6 + xbytes + 4096 * 3072 + 4096 * 32 * 2, timing="eager launches",
+            operands="bf16 activations rotated into fp6 tiles per call, weights converted once")
+        kernels["rotate_quant_int4_then_gemm_4096x4096x4096_g128"] = gemm_entry(
+            ms_ri, 4096, 4096 * 2048 * 2 + 8192 * 32 * 2 + 4096 * 4096 * 4 + xbytes + 4096 * 2048 + 4096 * 32 * 2,
+            timing="eager launches", operands="bf16 activations rotated into packed int4 per call")
+        del ad, sad, cg, a6, sta, w6, stw, xa
 
         # decode shapes (M = 16): a call is shorter than the Python call that
         # issues it, so calls are captured in a HIP graph and replayed.  "hot":

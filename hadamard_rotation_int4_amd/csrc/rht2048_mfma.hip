@@ -87,9 +87,11 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
   const int g = M[0].g, a4 = M[0].a4;
   const float tau = M[0].tau;
 
-  // LDS of this wave: two row stages (256 slots of 16 bytes per chunk) and
-  // one chunk of codes (fp6: the codes of a group of 4 rows, every chunk)
-  __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][2][CH * 256];
+  // LDS of this wave: NST row stages (256 slots of 16 bytes per chunk; a
+  // third stage measured slower for every output) and one chunk of codes
+  // (fp6: the codes of a group of 4 rows, every chunk)
+  constexpr int NST = 2;
+  __shared__ __attribute__((aligned(16))) u32x4 stage_lds[4][NST][CH * 256];
   __shared__ __attribute__((aligned(16))) u32x4 code_lds[4][BITS == 8 ? 128 : BITS == 6 ? CH * 400 : 64];
   // fp6: the group's scales, [group][row of the group] (fp16 or fp32 bits)
   constexpr int SES = SCALE_F16 ? 2 : 4;
@@ -123,8 +125,8 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
 #define HR_VMW(V) \
       case V: __builtin_amdgcn_s_waitcnt(((V) & 15) | (((V) >> 4) << 14) | 0x0F70); break;
       HR_VMW(0) HR_VMW(1) HR_VMW(2) HR_VMW(3) HR_VMW(4) HR_VMW(5) HR_VMW(6) HR_VMW(7) HR_VMW(8)
-      HR_VMW(10) HR_VMW(11) HR_VMW(12) HR_VMW(13) HR_VMW(14) HR_VMW(16) HR_VMW(20) HR_VMW(21)
-      HR_VMW(24) HR_VMW(32) HR_VMW(40)
+      HR_VMW(9) HR_VMW(10) HR_VMW(11) HR_VMW(12) HR_VMW(13) HR_VMW(14) HR_VMW(15) HR_VMW(16)
+      HR_VMW(20) HR_VMW(21) HR_VMW(24) HR_VMW(29) HR_VMW(32) HR_VMW(40)
 #undef HR_VMW
       default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // vmcnt(0)
     }
@@ -452,18 +454,24 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2
   };
   constexpr int LPR = 4 * CH;      // loads per row
   int64_t row = row_at(0);
-  if (row < rows) issue(row, 0);
-  if (row_at(1) < rows) issue(row_at(1), 1);
-  for (int st = 0, k = 0; row < rows; ++k, row = row_at(k), st ^= 1) {
+#pragma unroll
+  for (int i = 0; i < NST; ++i)
+    if (row_at(i) < rows) issue(row_at(i), i);
+  for (int st = 0, k = 0; row < rows; ++k, row = row_at(k), st = st + 1 == NST ? 0 : st + 1) {
     u32x4 b[CH][4];
-    // issued after this row's loads: the next row's loads (if any; issued
-    // before this row's loads only in the prologue), and the stores of the
-    // rows processed since this row's loads were issued (none, one, then two;
-    // a group's last fp6 flush is never followed by a wait)
-    const bool next = row_at(k + 1) < rows;
-    const int younger = (next ? LPR : 0) + (k >= 1 ? stores_at(k - 1) : 0) + (k >= 2 ? stores_at(k - 2) : 0);
+    // issued after this row's loads: the loads of the next NST - 1 rows (those
+    // that exist), and the stores of the rows processed since this row's
+    // loads were issued (up to NST of them; a wave's last fp6 flush is never
+    // followed by a wait)
+    int younger = 0;
+#pragma unroll
+    for (int i = 1; i < NST; ++i)
+      if (row_at(k + i) < rows) younger += LPR;
+#pragma unroll
+    for (int j = 1; j <= NST; ++j)
+      if (k - j >= 0) younger += stores_at(k - j);
     read_stage(st, younger, b);
-    if (row_at(k + 2) < rows) issue(row_at(k + 2), st);
+    if (row_at(k + NST) < rows) issue(row_at(k + NST), st);
     process(row, b);
     if (BITS == 6 && ((row & 3) == 3 || row + 1 == rows)) flush6(row & ~(int64_t)3);
   }
