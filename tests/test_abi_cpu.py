@@ -350,6 +350,44 @@ def _z(*shape, dtype=torch.float32):
     (lambda: hr.rotate_quant_w4a4_gemm(_z(16, 4096, dtype=torch.bfloat16), _z(64, 2048, dtype=torch.uint8),
                                        _z(64, 32, dtype=torch.float16), 128,
                                        signs=_z(2048, dtype=torch.int8)), ValueError, "signs: shape"),
+    # the tiled fp6 format: conversion, rotation straight into tiles, and the GEMM
+    (lambda: hr.w4a4_to_fp6(_z(4, 1000, dtype=torch.uint8)), ValueError, "multiple of 128"),
+    (lambda: hr.w4a4_to_fp6(_z(4, 1024, dtype=torch.int8)), TypeError, "codes"),
+    (lambda: hr.w4a4_to_fp6(_z(4, 1024, dtype=torch.uint8), out=_z(4, 1536, dtype=torch.uint8)),
+     ValueError, "out: shape"),
+    (lambda: hr.w4a4_to_fp6(_z(4, 1024, dtype=torch.uint8), group=128), ValueError, "go with scales"),
+    (lambda: hr.w4a4_to_fp6(_z(4, 1024, dtype=torch.uint8), _z(4, 16, dtype=torch.float16), 64),
+     ValueError, "group"),
+    (lambda: hr.w4a4_to_fp6(_z(4, 1024, dtype=torch.uint8), _z(4, 8, dtype=torch.float16), 128),
+     ValueError, "scales: shape"),
+    (lambda: hr.w4a4_to_fp6(_z(4, 1024, dtype=torch.uint8), _z(4, 16, dtype=torch.float16), 128,
+                            out_scales=_z(16, 4, dtype=torch.float16)), ValueError, "out_scales: shape"),
+    (lambda: hr.rotate_quant_fp6(_z(4, 2048), 128), TypeError, "x: dtype"),
+    (lambda: hr.rotate_quant_fp6(_z(4, 1024, dtype=torch.bfloat16), 128), ValueError, "n="),
+    (lambda: hr.rotate_quant_fp6(_z(4, 2048, dtype=torch.bfloat16), 64), ValueError, "group"),
+    (lambda: hr.rotate_quant_fp6(_z(4, 2048, dtype=torch.bfloat16), 128, signs=_z(1024, dtype=torch.int8)),
+     ValueError, "signs: shape"),
+    (lambda: hr.rotate_quant_fp6(_z(4, 2048, dtype=torch.bfloat16), 128, out=_z(4, 1536, dtype=torch.uint8)),
+     ValueError, "out: shape"),
+    (lambda: hr.rotate_quant_fp6(_z(4, 2048, dtype=torch.bfloat16), 128,
+                                 out_scales=_z(16, 128, dtype=torch.float32)), TypeError, "out_scales: dtype"),
+    (lambda: hr.rotate_quant_fp6(_z(4, 2048, dtype=torch.bfloat16), 128, scale_dtype=torch.bfloat16),
+     TypeError, "scale_dtype"),
+    (lambda: hr.w4a4_gemm_fp6(_z(128, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float16),
+                              _z(128, 1536, dtype=torch.uint8), _z(8, 128, dtype=torch.float16), 128, 4),
+     ValueError, "K\\*3/4"),
+    (lambda: hr.w4a4_gemm_fp6(_z(128, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float16),
+                              _z(128, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float32), 128, 4),
+     TypeError, "share a dtype"),
+    (lambda: hr.w4a4_gemm_fp6(_z(64, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float16),
+                              _z(128, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float16), 128, 4),
+     ValueError, "a_f6: shape"),
+    (lambda: hr.w4a4_gemm_fp6(_z(128, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float16),
+                              _z(128, 768, dtype=torch.uint8), _z(4, 128, dtype=torch.float16), 128, 4),
+     ValueError, "w_scales: shape"),
+    (lambda: hr.w4a4_gemm_fp6(_z(128, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float16),
+                              _z(128, 768, dtype=torch.uint8), _z(8, 128, dtype=torch.float16), 128, 4,
+                              out=_z(4, 64)), ValueError, "out: shape"),
 ])
 def test_binding_rejects_bad_tensors(call, exc, msg):
     with pytest.raises(exc, match=msg):
