@@ -214,3 +214,33 @@ def test_rotate_quant_fp6_then_gemm(M):
                                                   return_sums=True)
     check_gemm(c.cpu().numpy(), c_ref, bound, acc.cpu().numpy(), acc_ref)
     assert torch.isfinite(c).all()
+
+
+def _sample(rows, k, seed=0):
+    idx = np.random.default_rng(seed).choice(rows, size=k, replace=False)
+    return np.unique(np.concatenate([idx, [0, rows - 1]]))
+
+
+@pytest.mark.parametrize("rows,n", [(65536, 2048), (4096, 4096)])
+def test_rotate_quant_fp6_fullsize(rows, n):
+    """The headline shape (bf16 65536 x 2048) and the GEMM's activation
+    shape (4096 x 4096), G = 128, fp16 scales: every row's decoded tile codes
+    and every transposed scale equal the int4 entry's bit for bit, and a
+    seeded sample of rows (plus the first and last) matches the oracle."""
+    hr = _hr()
+    ri = hr_inputs.rht_inputs(rows=rows, n=n)
+    x, d = ri.x.to(DEV), _t(ri.signs)
+    tiles, st = hr.rotate_quant_fp6(x, 128, d)
+    codes4, scales4 = hr.rotate_quant_int4(x, 128, d)
+    tiles_np, c4 = tiles.cpu().numpy(), codes4.cpu().numpy()
+    for r0 in range(0, rows, 4096):
+        nr = min(4096, rows - r0)
+        q = decode_fp6_tiles_np(tiles_np[r0:r0 + (nr + 127) // 128 * 128], nr)
+        np.testing.assert_array_equal(q, oracle.quant.unpack_int4(c4[r0:r0 + nr]))
+    sc = st.cpu().numpy()[:, :rows].T
+    np.testing.assert_array_equal(sc.view(np.uint16), scales4.cpu().numpy().view(np.uint16))
+    sample = _sample(rows, 64, seed=n)
+    q = np.concatenate([decode_fp6_tiles_np(tiles_np[r // 128 * 128:(r // 128 + 1) * 128], r % 128 + 1)[-1:]
+                        for r in sample])
+    y64 = oracle.hadamard.rht(ri.x[sample].float().numpy(), ri.signs)
+    check_quant(oracle.quant.pack_int4(q), sc[sample], y64, 128, "f16")
