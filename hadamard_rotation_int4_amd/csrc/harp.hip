@@ -15,11 +15,13 @@
 // table is coefficient-major per stage, [b][b][d/b]: coefficient (r, q) of
 // block c at (r b + q) d/b + c, so the lanes of a wave, which own consecutive
 // blocks, read each coefficient as one contiguous 256-byte run.
-// harp_apply_kernel: a persistent workgroup keeps R rows in LDS and runs
-// every stage over them; each thread takes blocks c = tid, tid + 1024, ...,
-// holds the block's b^2 coefficients in registers while it maps that block of
-// all R rows, so the coefficient table (d * sum b_t floats, read from L2) is
-// fetched once per R rows.  Quantization (int4, per group) is fused at the end.
+// harp_apply_kernel: a persistent workgroup keeps R rows in LDS (loaded by
+// LDS-DMA, every load in flight at once) and runs every stage over them; each
+// thread takes blocks c = tid, tid + 1024, ..., holds the block's b^2
+// coefficients in registers while it maps that block of all R rows, so the
+// coefficient table (d * sum b_t floats, read from L2) is fetched once per R
+// rows, and requests its first block's coefficients before the barrier that
+// opens the stage.  Quantization (int4, per group) is fused at the end.
 #include "hr_internal.h"
 #include "hr_device.h"
 #include "quant_lds.h"
@@ -29,6 +31,11 @@ namespace hr {
 // 1024 threads: the radix-8 stages of d = 5120 (640 blocks) and its radix-5
 // stage (1024 blocks) each take one round (with 512 threads the radix-8 stages took two rounds: 96 us against 89 us)
 constexpr int kHarpThreads = 1024;
+
+// 16-byte global -> LDS copy (LDS-DMA: lane i's 16 bytes land at lp + 16 i)
+__device__ __forceinline__ void harp_lds_load16(const void* gp, void* lp) {
+  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+}
 
 // LDS position of in-row element i when 64 divides d: bits 2-5 XORed with
 // bits 6-9 of i, a permutation inside every aligned block of 64 elements.
@@ -112,42 +119,63 @@ __global__ __launch_bounds__(256) void harp_blocks_kernel(HarpSchedule sc, const
     }
 }
 
-// Map every block c of one stage (radix B) over the R rows in LDS.
+// The b^2 coefficients of block c (transposed for the inverse).
+template <int B>
+__device__ __forceinline__ void harp_coeffs(float (&m)[B][B], const float* __restrict__ blk, int c, int nb,
+                                            bool inverse) {
+  const float* src = blk + c;
+  if (inverse) {
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+#pragma unroll
+      for (int j = 0; j < B; ++j) m[i][j] = src[(int64_t)(j * B + i) * nb];
+  } else {
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+#pragma unroll
+      for (int j = 0; j < B; ++j) m[i][j] = src[(int64_t)(i * B + j) * nb];
+  }
+}
+
+// Map block c of one stage over the R rows in LDS.
+template <int B>
+__device__ __forceinline__ void harp_block(const float (&m)[B][B], float* lds, int d, int R, int S, int c,
+                                           bool swz) {
+  const int lo = c % S, hi = c / S;
+  const int base = lo + S * B * hi;
+  int pos[B];
+#pragma unroll
+  for (int q = 0; q < B; ++q) pos[q] = hswz(base + q * S, swz);
+  for (int r = 0; r < R; ++r) {
+    float* row = lds + r * d;
+    float v[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) v[q] = row[pos[q]];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < B; ++q) acc = fmaf(m[i][q], v[q], acc);
+      row[pos[i]] = acc;
+    }
+  }
+}
+
+// One stage (radix B) over the R rows in LDS.  A thread's first block's
+// coefficients are requested before the barrier that ends the previous stage
+// (or the row loads), so their L2 latency overlaps the other waves' work
+// (prefetching the further blocks of b = 2 as well measured no faster).
 template <int B>
 __device__ __forceinline__ void harp_stage(float* lds, int d, int R, int S, int nb,
                                            const float* __restrict__ blk, bool inverse, bool swz) {
-  for (int c = threadIdx.x; c < nb; c += kHarpThreads) {
-    float m[B][B];
-    const float* src = blk + c;
-    if (inverse) {
-#pragma unroll
-      for (int i = 0; i < B; ++i)
-#pragma unroll
-        for (int j = 0; j < B; ++j) m[i][j] = src[(int64_t)(j * B + i) * nb];
-    } else {
-#pragma unroll
-      for (int i = 0; i < B; ++i)
-#pragma unroll
-        for (int j = 0; j < B; ++j) m[i][j] = src[(int64_t)(i * B + j) * nb];
-    }
-    const int lo = c % S, hi = c / S;
-    const int base = lo + S * B * hi;
-    int pos[B];
-#pragma unroll
-    for (int q = 0; q < B; ++q) pos[q] = hswz(base + q * S, swz);
-    for (int r = 0; r < R; ++r) {
-      float* row = lds + r * d;
-      float v[B];
-#pragma unroll
-      for (int q = 0; q < B; ++q) v[q] = row[pos[q]];
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int q = 0; q < B; ++q) acc = fmaf(m[i][q], v[q], acc);
-        row[pos[i]] = acc;
-      }
-    }
+  const int c0 = threadIdx.x;
+  float m[B][B];
+  if (c0 < nb) harp_coeffs<B>(m, blk, c0, nb, inverse);
+  __syncthreads();
+  if (c0 < nb) harp_block<B>(m, lds, d, R, S, c0, swz);
+  for (int c = c0 + kHarpThreads; c < nb; c += kHarpThreads) {
+    harp_coeffs<B>(m, blk, c, nb, inverse);
+    harp_block<B>(m, lds, d, R, S, c, swz);
   }
 }
 
@@ -160,14 +188,22 @@ __global__ __launch_bounds__(kHarpThreads) void harp_apply_kernel(HarpArgs a) {
   for (int64_t rg = blockIdx.x; rg < ngroups; rg += gridDim.x) {
     const int64_t r0 = rg * R;
     const int nr = (int)(a.rows - r0 < R ? a.rows - r0 : R);
-    // load nr rows (float4; d is a multiple of 4)
-    const int q4 = d / 4;
-    for (int i = tid; i < nr * q4; i += kHarpThreads) {
-      const int r = i / q4, k = i - r * q4;
-      *reinterpret_cast<float4*>(lds + r * d + hswz(4 * k, swz)) =
-          reinterpret_cast<const float4*>(a.x + (r0 + r) * d)[k];
+    // load nr rows (float4; d is a multiple of 4) by LDS-DMA, 1 KB of LDS
+    // per instruction and no registers held: LDS float4 p (row r, in-row k)
+    // takes the row's float4 whose swizzled place is k (the swizzle is its
+    // own inverse); every load is in flight before the barrier's wait
+    const int q4 = d / 4, npc = nr * q4;
+    const int wv = tid >> 6, ln = tid & 63;
+    const float4* src = reinterpret_cast<const float4*>(a.x + r0 * d);
+    for (int u = wv; u * 64 < npc; u += kHarpThreads / 64) {
+      const int p = 64 * u + ln;
+      if (p < npc) {
+        const int r = p / q4, k = p - r * q4;
+        harp_lds_load16(src + r * q4 + (hswz(4 * k, swz) >> 2), lds + 256 * u);
+      }
     }
-    __syncthreads();
+    // (each stage starts with the barrier that waits for these loads or the
+    // previous stage's writes)
     for (int s = 0; s < a.sc.nstages; ++s) {
       const int t = a.inverse ? a.sc.nstages - 1 - s : s;
       const int b = a.sc.radix[t], S = a.sc.stride[t], nb = d / b;
@@ -181,10 +217,10 @@ __global__ __launch_bounds__(kHarpThreads) void harp_apply_kernel(HarpArgs a) {
         case 7: harp_stage<7>(lds, d, nr, S, nb, blk, a.inverse, swz); break;
         default: harp_stage<8>(lds, d, nr, S, nb, blk, a.inverse, swz); break;
       }
-      __syncthreads();
     }
+    __syncthreads();
     if (a.y) {
-      for (int i = tid; i < nr * q4; i += kHarpThreads) {
+      for (int i = tid; i < npc; i += kHarpThreads) {
         const int r = i / q4, k = i - r * q4;
         reinterpret_cast<float4*>(a.y + (r0 + r) * d)[k] =
             *reinterpret_cast<const float4*>(lds + r * d + hswz(4 * k, swz));
@@ -212,11 +248,14 @@ hipError_t launch_harp_apply(HarpArgs a, hipStream_t s) {
   // workgroups, 120 us)
   int R = (int)(40960 / a.d);
   if (R > 8) R = 8;
+  // the row loads fill LDS in whole 1 KB runs: keep the rounded-up group
+  // inside the 160 KB
+  while (R > 1 && ((int64_t)R * a.d + 255) / 256 * 256 > 40960) --R;
   if (R < 1) R = 1;
   a.rows_per_group = R;
   const int64_t ngroups = (a.rows + R - 1) / R;
   const int64_t grid = ngroups < 512 ? ngroups : 512;
-  const size_t lds = sizeof(float) * (size_t)R * a.d;
+  const size_t lds = sizeof(float) * (((size_t)R * a.d + 255) / 256 * 256);
   // more than 64 KB of dynamic LDS must be allowed explicitly (160 KB per
   // workgroup on gfx950)
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(harp_apply_kernel),
