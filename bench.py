@@ -39,6 +39,15 @@ TRAFFIC_FILE = os.path.join(PROFILES, "rht_quant_bf16_65536x2048_g128.traffic.js
 COPY_BYTES = 512 * 1024 * 1024       # calibration copy: reads and writes this many bytes
 
 
+class _Progress(dict):
+    """The kernel table; each entry also prints a progress line on stderr
+    (stdout carries only the one JSON line)."""
+
+    def __setitem__(self, k, v):
+        super().__setitem__(k, v)
+        print(f"bench.py: {k} done", file=sys.stderr, flush=True)
+
+
 def main_kernel_hash():
     h = hashlib.sha256()
     for name in MAIN_KERNEL_SOURCES:
@@ -239,8 +248,8 @@ def main(argv=None):
     if args.summarize_profile:
         return summarize_profile(args.summarize_profile)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this path runs on one GPU only (rows are independent; see DESIGN.md "
-              "for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py: this path runs on one GPU only (rows are independent, so several GPUs "
+              "would each take their own rows); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
@@ -313,8 +322,8 @@ def main(argv=None):
         how = "eager launches"
     alg = rht_alg_bytes(ROWS, N, GROUP)
     gbs = alg / (ms * 1e-3) / 1e9
-    kernels = {"rht_quant_bf16_65536x2048_g128": _entry(ms, **{"GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
-                                                               "bytes": alg, "timing": how})}
+    kernels = _Progress({"rht_quant_bf16_65536x2048_g128": _entry(ms, **{"GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                                                                         "bytes": alg, "timing": how})})
 
     def hbm_entry(t, byts, **kw):
         return _entry(t, **{"GB/s": byts / t / 1e6, "frac_hbm": byts / t / 1e6 / HBM_PEAK_GBS,
