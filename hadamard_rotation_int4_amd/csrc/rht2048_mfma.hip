@@ -47,10 +47,13 @@ namespace hr {
 // instances (36 KB of LDS each; 61.9 us against 65.0 us with two, same box,
 // bf16 65536 x 2048, G = 128), two for the fp32 output and the 4096-point
 // rows, whose 68 KB would not fit three times, and one for the fp32 output of
-// 4096-point rows (its registers leave room for one wave per SIMD).
-constexpr int kMfmaBlocksPerCu = 2;
-template <bool OUT_F32, int CH>
-constexpr int mfma_blocks_per_cu() { return (OUT_F32 && CH == 2) ? 1 : (OUT_F32 || CH == 2) ? 2 : 3; }
+// 4096-point rows (its registers leave room for one wave per SIMD).  The fp6
+// output's group staging takes 59 KB (2048-point rows: two fit) or 117 KB
+// (4096-point rows: one fits).
+template <bool OUT_F32, int CH, int BITS>
+constexpr int mfma_blocks_per_cu() {
+  return BITS == 6 ? (CH == 2 ? 1 : 2) : (OUT_F32 && CH == 2) ? 1 : (OUT_F32 || CH == 2) ? 2 : 3;
+}
 
 // 16-byte global -> LDS copy (the builtin sits in a device function: used
 // directly in a kernel template it can cost the instance its host stub)
@@ -59,7 +62,7 @@ __device__ __forceinline__ void mfma_lds_load16(const void* gp, void* lp) {
 }
 
 template <int G, bool SCALE_F16, bool OUT_F32, int BITS, int CH = 1>
-__global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH>())) void rht2048_mfma_kernel(
+__global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) void rht2048_mfma_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ signs, int64_t rows,
     float* __restrict__ yout, uint8_t* __restrict__ codes, void* __restrict__ scales, float norm) {
   static_assert(CH == 1 || CH == 2, "rows of one or two 2048-point chunks");
@@ -481,7 +484,8 @@ template <int G, bool SCALE_F16, bool OUT_F32, int BITS = 4>
 static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
   // 4 waves per block, one row per wave (fp6: a group of 4 rows per wave)
   int64_t blocks = BITS == 6 ? (a.rows + 15) / 16 : (a.rows + 3) / 4;
-  const int64_t cap = 256 * (a.p == 4096 ? mfma_blocks_per_cu<OUT_F32, 2>() : mfma_blocks_per_cu<OUT_F32, 1>());
+  const int64_t cap =
+      256 * (a.p == 4096 ? mfma_blocks_per_cu<OUT_F32, 2, BITS>() : mfma_blocks_per_cu<OUT_F32, 1, BITS>());
   if (blocks > cap) blocks = cap;
   if (a.p == 4096)
     hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS, 2>), dim3((unsigned)blocks),
@@ -518,7 +522,7 @@ bool launch_rht2048_mfma(const RhtArgs& a, hipStream_t s) {
   // n = 4096 with fewer rows than one resident wave per row: the mixed-radix
   // kernel, which spreads each row over eight waves, has the lower latency
   // (16 rows: 3.3 us against 5.0 us)
-  if (a.p == 4096 && a.rows < 256 * kMfmaBlocksPerCu * 4) return false;
+  if (a.p == 4096 && a.rows < 256 * mfma_blocks_per_cu<false, 2, 4>() * 4) return false;
   const float norm = (float)(1.0 / sqrt((double)a.p));
   if (a.y && !a.codes) {
     launch_mfma<0, false, true>(a, norm, s);

@@ -244,3 +244,24 @@ def test_rotate_quant_fp6_fullsize(rows, n):
                         for r in sample])
     y64 = oracle.hadamard.rht(ri.x[sample].float().numpy(), ri.signs)
     check_quant(oracle.quant.pack_int4(q), sc[sample], y64, 128, "f16")
+
+
+@pytest.mark.parametrize("rows,n", [(5, 2048), (131, 4096)])
+def test_rotate_quant_fp6_tiny_fp32_scales(rows, n):
+    """Delta rows c e_0 with c = 2^-120 (bf16): every rotated value is
+    +-c / sqrt(n), the fp32 scale is below 2^-128 (its reciprocal would
+    overflow; the quantizer rescales by 2^64) and every code is +-7; the
+    tiles hold those codes and the transposed scales match the oracle's."""
+    hr = _hr()
+    d = hr_inputs.sign_vector(np.random.default_rng(502), n)
+    x = np.zeros((rows, n), dtype=np.float32)
+    x[:, 0] = np.float32(2.0 ** -120)
+    x[1::2, 0] *= -1
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    tiles, st = hr.rotate_quant_fp6(xt.to(DEV), 128, _t(d), scale_dtype=torch.float32)
+    q = decode_fp6_tiles_np(tiles.cpu().numpy(), rows)
+    s = st.cpu().numpy()[:, :rows].T.copy()
+    y64 = oracle.hadamard.rht(x, d)
+    assert np.all(s < 2.0 ** -128) and np.all(s > 0)
+    assert np.all(np.abs(q) == 7)
+    check_quant(oracle.quant.pack_int4(q), s, y64, 128, "f32")
