@@ -17,11 +17,6 @@
 #include "hr_internal.h"
 #include "fwht2048.h"
 
-// Persistent grid of the row kernel: blocks of 4 waves per compute unit.
-#ifndef HR_RHT2048_BLOCKS_PER_CU
-#define HR_RHT2048_BLOCKS_PER_CU 8
-#endif
-
 namespace hr {
 
 template <bool IN_BF16, int G, bool SCALE_F16, bool OUT_F32>
@@ -155,8 +150,19 @@ static void launch_one(const RhtArgs& a, float norm, hipStream_t s) {
     return;
   }
   if (a.m == 1) {
+    // persistent grid: as many 4-wave blocks as are resident at once (a block
+    // past that would only start when another has finished all its rows)
+    static const int per_cu = [] {
+      int nb = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &nb, reinterpret_cast<const void*>(&rht2048_kernel<IN_BF16, G, SCALE_F16, OUT_F32>), 256, 0) !=
+              hipSuccess ||
+          nb < 1)
+        nb = 1;
+      return nb;
+    }();
     int64_t blocks = (a.rows + 3) / 4;   // one wave per row, 4 waves per block
-    const int64_t cap = 256 * HR_RHT2048_BLOCKS_PER_CU;
+    const int64_t cap = 256 * (int64_t)per_cu;
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL((rht2048_kernel<IN_BF16, G, SCALE_F16, OUT_F32>), dim3((unsigned)blocks),
                        dim3(256), 0, s, a.x, a.signs, a.rows, a.y, a.codes, a.scales, norm);
