@@ -38,7 +38,9 @@
 //     the next block's in LDS (384 would put the 16 blocks a staging store
 //     touches in the same banks).  The fields come from the fp32 -> fp6
 //     pack conversion of the exact integer codes with scale 8 (code / 8 is
-//     an e2m3 value), 32 codes per instruction.
+//     an e2m3 value), 32 codes per instruction.  The scales are staged per
+//     group too and leave transposed, one 8-byte (fp16) or 16-byte (fp32)
+//     piece per group of quantization and 4 rows.
 #include "mfma2048.h"
 
 namespace hr {
