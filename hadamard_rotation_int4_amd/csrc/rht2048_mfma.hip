@@ -72,13 +72,10 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
   constexpr int N = CH * P;        // row
   const int lane = threadIdx.x & 63;
   const int wib = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  // fp6 output: workgroups are dealt to the 8 XCDs in turn, so block b
-  // takes place (b % 8) (blocks / 8) + b / 8: each XCD then covers runs of
-  // consecutive rows, and the lines of a tile or of the transposed scales
-  // are written from one L2
-  int64_t bid = blockIdx.x;
-  if (BITS == 6 && (gridDim.x & 7) == 0) bid = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int64_t wave = bid * (blockDim.x >> 6) + wib;
+  // (an XCD-aware order for the fp6 output, each XCD taking runs of
+  // consecutive rows, measured 83.7 against 76.2 us with HBM-resident
+  // buffers, bf16 65536 x 2048)
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + wib;
   const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
   // the k-th row of this wave: rows wave + k nwaves, or for fp6 output groups
   // of 4 consecutive rows (group wave + (k / 4) nwaves)
