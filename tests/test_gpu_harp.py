@@ -153,7 +153,8 @@ def test_harp_4096x5120_sampled():
 
 @pytest.mark.parametrize("radices,rows", [((8, 8, 8, 5, 2), 131), ((4, 5, 3, 2), 97), ((2,) * 6, 64),
                                           ((7, 4, 2), 33), ((6, 4), 40), ((3, 3, 4), 50),
-                                          ((8, 8, 8, 8), 21), ((2, 2), 9)])
+                                          ((8, 8, 8, 8), 21), ((2, 2), 9),
+                                          ((8, 8, 8, 8, 4), 5)])   # d = 16384: 2 rows a group, one ragged
 def test_harp_theta_to_output(radices, rows):
     """Forward and inverse output from theta, against the oracle's fp64 blocks
     at 2e-5 x row max; the oracle's fp32-stored blocks at the same bound."""
