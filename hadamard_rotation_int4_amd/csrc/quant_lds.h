@@ -4,6 +4,7 @@
 #pragma once
 
 #include "hr_device.h"
+#include "fwht2048.h"
 
 namespace hr {
 
@@ -45,10 +46,13 @@ __device__ __forceinline__ void quant_row_from_lds(const float* vals, float norm
 // (values already normalised), spread over the whole workgroup: G / 4 lanes
 // share a group, each owning 4 consecutive values (one 16-byte LDS read, no
 // bank conflicts), so a wave covers 256 / G groups at a time.  The group
-// absmax is reduced with shuffles inside the lane group; codes are taken
-// against the stored scale with IEEE division and ties away from zero, and
-// each lane stores its 4 codes as one 16-bit word.  pos maps an in-row index
-// (a multiple of 4) to its LDS position (groups of 4 contiguous).
+// absmax is reduced by DPP and permlane steps inside the lane group; the scale is the
+// correctly rounded absmax / 7, and the codes are the fused kernels': y times
+// the reciprocal of the stored scale, rounded by the magic-number fma (the
+// decision differs from y / s with ties away from zero only within a few
+// ulps of a midpoint), clamped to +-7; each lane stores its 4 codes as one
+// 16-bit word.  pos maps an in-row index (a multiple of 4) to its LDS position
+// (groups of 4 contiguous).
 struct IdentityPos {
   __device__ int operator()(int i) const { return i; }
 };
@@ -68,16 +72,38 @@ __device__ __forceinline__ void quant_rows_from_lds(const float* vals, int pitch
     const int r = rg / gpr, g = rg - r * gpr;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) v = *reinterpret_cast<const float4*>(vals + r * pitch + pos(g * G + 4 * l));
-    float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    for (int o = lpg >> 1; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    // group absmax over the lpg lanes: DPP steps inside a 16-lane row, then
+    // row pairs and halves by permlane swaps (non-negative values compare as
+    // unsigned bit patterns)
+    uint32_t mu = __float_as_uint(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    mu = umax_dpp<kQuadXor1>(mu);
+    mu = umax_dpp<kQuadXor2>(mu);
+    mu = umax_dpp<kRowHalfMirror>(mu);
+    if (lpg >= 16) mu = umax_dpp<kRowMirror>(mu);
+    if (lpg >= 32) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(mu, mu, false, false);
+      mu = sw[0] > sw[1] ? sw[0] : sw[1];
+    }
+    if (lpg >= 64) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(mu, mu, false, false);
+      mu = sw[0] > sw[1] ? sw[0] : sw[1];
+    }
+    const float mx = __uint_as_float(mu);
     if (!live) continue;
-    const float s32 = mx / 7.0f;
+    const float s32 = div_const<7>(mx);
     const float sc = scale_f16 ? (float)(_Float16)s32 : s32;
     const int64_t row = row0 + r;
     if (l == 0) store_scale(scales, row * gpr + g, s32, scale_f16);
-    const int q0 = quant_code_exact(v.x, sc), q1 = quant_code_exact(v.y, sc);
-    const int q2 = quant_code_exact(v.z, sc), q3 = quant_code_exact(v.w, sc);
-    const uint16_t w = (uint16_t)((q0 & 0xF) | ((q1 & 0xF) << 4) | ((q2 & 0xF) << 8) | ((q3 & 0xF) << 12));
+    // an fp32 scale below 2^-100 would overflow its reciprocal: y and s are
+    // then both taken x 2^64 (exact; same quotients)
+    const float up = (!scale_f16 && sc < 0x1p-100f) ? 0x1p64f : 1.0f;
+    const float k = sc > 0.0f ? __builtin_amdgcn_rcpf(sc * up) : 0.0f;
+    // q + 1.5 * 2^23 + 8 holds q + 8 in its low nibble (ties to even)
+    constexpr float MQ = 12582920.0f;
+    auto nib = [&](float y) -> uint32_t {
+      return __float_as_uint(__builtin_amdgcn_fmed3f(fmaf(y * up, k, MQ), MQ - 7.0f, MQ + 7.0f)) & 0xFu;
+    };
+    const uint16_t w = (uint16_t)((nib(v.x) | (nib(v.y) << 4) | (nib(v.z) << 8) | (nib(v.w) << 12)) ^ 0x8888u);
     reinterpret_cast<uint16_t*>(codes + row * (n / 2) + g * (G / 2))[l] = w;
   }
 }

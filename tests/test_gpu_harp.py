@@ -93,6 +93,23 @@ def test_harp_apply_quant(group, scale_mode):
     assert torch.equal(c2, codes) and torch.equal(s2, scales)
 
 
+@pytest.mark.parametrize("group", [128, 32])
+def test_harp_quant_tiny_fp32_scales(group):
+    """Rows scaled by 2^-120: every fp32 group scale is below 2^-100, where
+    its reciprocal would overflow; the quantizer takes values and scale
+    x 2^64 (exact) and the codes still match the oracle's."""
+    hr = _hr()
+    hi = hr_inputs.harp_inputs(rows=9, seed=84 + group)
+    x = (hi.x.astype(np.float64) * 2.0 ** -120).astype(np.float32)
+    blk = _gpu_blocks(hi)
+    _, codes, scales = hr.harp_apply(_t(x), hi.radices, blk, want_y=False, group=group,
+                                     scale_dtype=torch.float32)
+    y64 = H.apply(x.astype(np.float64), hi.radices, _split(blk.cpu().numpy(), hi.radices))
+    s = scales.cpu().numpy()
+    assert np.all(s < 2.0 ** -100) and np.all(s > 0)
+    check_quant(codes.cpu().numpy(), s, y64, group, "f32")
+
+
 def test_harp_zero_theta_is_hadamard():
     hr = _hr()
     radices = (4, 8, 2, 8)
