@@ -78,10 +78,16 @@ struct Mfma2048 {
   float tau;              // sign of the lane's results after the DPP stages
 };
 
+// The chunk A(q) whose B operands lane q of a DPP row holds (a GF(2) relabel
+// of the 16 positions that makes every H_16 partner a DPP pattern).
+__device__ __forceinline__ int mfma2048_a4(int q) {
+  return (q & 12) | ((q ^ (q >> 2)) & 1) | ((((q >> 1) ^ (q >> 2)) & 1) << 1);
+}
+
 // signs: the chunk's 2048 signs (int8 +-1) or null (all +1).
 __device__ __forceinline__ void mfma2048_init(Mfma2048& M, int lane, const int8_t* signs) {
   const int q = lane & 15, g = lane >> 4;
-  const int a4 = (q & 12) | ((q ^ (q >> 2)) & 1) | ((((q >> 1) ^ (q >> 2)) & 1) << 1);
+  const int a4 = mfma2048_a4(q);
   M.q = q;
   M.g = g;
   M.a4 = a4;

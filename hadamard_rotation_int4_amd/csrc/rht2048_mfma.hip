@@ -16,11 +16,13 @@
 // H_2 stage is a lane-local sum and difference.
 //
 //   Staging: each wave streams its rows through two 4 KB LDS stages filled by
-//     global_load_lds_dwordx4 (two rows in flight per wave without holding
-//     registers).  Load j < 4, lane i fetches the 16-byte piece (chunk i & 15,
-//     piece 4 j + (i >> 4) of the chunk), so global reads come in 64-byte
-//     runs and the 16 pieces a lane group needs for one MFMA are consecutive
-//     LDS slots (no bank conflicts).
+//     nontemporal global_load_lds_dwordx4 (two rows in flight per wave
+//     without holding registers).  Load j < 4 of a 2048-point chunk covers
+//     its bytes 1024 j .. 1024 j + 1023, whole cache lines; lane i fetches
+//     piece u of 128-element chunk 4 j + h (h = i >> 4, u = i - 4 j - h mod
+//     16), so chunk a, piece p lands in LDS slot 16 a + (p + a mod 16) and
+//     the 16 pieces a lane group reads for one MFMA (piece 4 s + g of the 16
+//     chunks) fall in 16 different bank groups.
 //   Codes: a lane owns four runs of 8 consecutive outputs; they are staged
 //     through LDS (swizzled, conflict-free) and written as contiguous 1 KB
 //     runs, one per store instruction (one per int4 row, two per int8 row).
@@ -57,10 +59,13 @@ constexpr int mfma_blocks_per_cu() {
   return BITS == 6 ? (CH == 2 ? 1 : 2) : (OUT_F32 && CH == 2) ? 1 : (OUT_F32 || CH == 2) ? 2 : 3;
 }
 
-// 16-byte global -> LDS copy (the builtin sits in a device function: used
-// directly in a kernel template it can cost the instance its host stub)
+// 16-byte global -> LDS copy, nontemporal (the builtin sits in a device
+// function: used directly in a kernel template it can cost the instance its
+// host stub).  With HBM-resident input (bf16 65536 x 2048, three buffer
+// sets, same box) the nontemporal hint on whole-line loads took the kernel
+// from 63.8 to 62.9 us; on the earlier 64-byte runs it had cost 0.7 us.
 __device__ __forceinline__ void mfma_lds_load16(const void* gp, void* lp) {
-  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 2);
 }
 
 template <int G, bool SCALE_F16, bool OUT_F32, int BITS, int CH = 1>
@@ -83,11 +88,11 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
     if (BITS == 6) return 4 * (wave + (int64_t)(k >> 2) * nwaves) + (k & 3);
     return wave + (int64_t)k * nwaves;
   };
+  // (initialized after the first rows' loads are issued, so that the sign
+  // loads and the setup overlap them: 62.9 -> 60.6 us, same box)
   Mfma2048 M[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) mfma2048_init(M[c], lane, signs ? signs + c * P : nullptr);
-  const int g = M[0].g, a4 = M[0].a4;
-  const float tau = M[0].tau;
+  const int g = lane >> 4, a4 = mfma2048_a4(lane & 15);
+  const float tau = (__builtin_popcount(a4) & 1) ? -1.0f : 1.0f;
 
   // LDS of this wave: NST row stages (256 slots of 16 bytes per chunk; a
   // third stage measured slower for every output) and one chunk of codes
@@ -100,26 +105,33 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
   __shared__ __attribute__((aligned(16))) uint8_t scale_lds[4][BITS == 6 ? 4 * (N / G) * SES : 16];
   // fp32 output: this wave's 8 KB output row, staged so it leaves as 1 KB stores
   __shared__ __attribute__((aligned(16))) f32x4 out_lds[OUT_F32 ? 4 : 1][OUT_F32 ? 512 : 1];
-  // element offset of this lane's piece within a row, per load j: + 32 j
-  const int lane_src = 128 * (lane & 15) + 8 * (lane >> 4);
+  // element offset within a chunk of this lane's piece for load j
+  int lane_src[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = lane >> 4, u = ((lane & 15) - 4 * j - h) & 15;
+    lane_src[j] = 512 * j + 128 * h + 8 * u;
+  }
   auto issue = [&](int64_t row, int st) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const uint16_t* base = x + row * N + c * P + lane_src;
+      const uint16_t* base = x + row * N + c * P;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        mfma_lds_load16(base + 32 * j, &stage_lds[wib][st][256 * c + 64 * j]);
+        mfma_lds_load16(base + lane_src[j], &stage_lds[wib][st][256 * c + 64 * j]);
     }
   };
-  // B operands of one row from stage st: lane (q, g) takes slot 64 s + 16 g +
-  // A(q) of each chunk for K-step s.  First a wait for the stage's loads:
+  // B operands of one row from stage st: lane (q, g) takes piece 4 s + g of
+  // chunk A(q), slot 16 A(q) + (4 s + g + A(q) mod 16), for K-step s.  First a wait for the stage's loads:
   // vector-memory operations complete in issue order (loads and stores
   // alike), so it is a wait until at most `younger` operations are
   // outstanding, where younger counts what this wave issued after the
   // stage's loads -- the next row's loads and the stores of the rows
   // processed since (see the loop).  Then one asm block reads the stage and
   // waits for its own results.
-  const uint32_t rd_lane = 16u * (uint32_t)(16 * g + a4);
+  uint32_t rd_lane[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rd_lane[k] = 16u * (uint32_t)(16 * a4 + ((a4 + 4 * k + g) & 15));
   auto read_stage = [&](int st, int younger, u32x4 (&b)[CH][4]) {
     // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
     // left at their maxima (no wait)
@@ -132,23 +144,23 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
 #undef HR_VMW
       default: __builtin_amdgcn_s_waitcnt(0x0F70); break;   // vmcnt(0)
     }
-    const uint32_t addr = (uint32_t)(uintptr_t)&stage_lds[wib][st][0] + rd_lane;
+    const uint32_t sb = (uint32_t)(uintptr_t)&stage_lds[wib][st][0];
     if (CH == 1)
-      asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
-                   "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+      asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+                   "ds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
                    "s_waitcnt lgkmcnt(0)"
                    : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3])
-                   : "v"(addr)
+                   : "v"(sb + rd_lane[0]), "v"(sb + rd_lane[1]), "v"(sb + rd_lane[2]), "v"(sb + rd_lane[3])
                    : "memory");
     else
-      asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
-                   "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
-                   "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %8 offset:5120\n\t"
-                   "ds_read_b128 %6, %8 offset:6144\n\tds_read_b128 %7, %8 offset:7168\n\t"
+      asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\t"
+                   "ds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+                   "ds_read_b128 %4, %8 offset:4096\n\tds_read_b128 %5, %9 offset:4096\n\t"
+                   "ds_read_b128 %6, %10 offset:4096\n\tds_read_b128 %7, %11 offset:4096\n\t"
                    "s_waitcnt lgkmcnt(0)"
                    : "=v"(b[0][0]), "=v"(b[0][1]), "=v"(b[0][2]), "=v"(b[0][3]),
                      "=v"(b[CH - 1][0]), "=v"(b[CH - 1][1]), "=v"(b[CH - 1][2]), "=v"(b[CH - 1][3])
-                   : "v"(addr)
+                   : "v"(sb + rd_lane[0]), "v"(sb + rd_lane[1]), "v"(sb + rd_lane[2]), "v"(sb + rd_lane[3])
                    : "memory");
   };
 
@@ -459,12 +471,16 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
 #pragma unroll
   for (int i = 0; i < NST; ++i)
     if (row_at(i) < rows) issue(row_at(i), i);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) mfma2048_init(M[c], lane, signs ? signs + c * P : nullptr);
   for (int st = 0, k = 0; row < rows; ++k, row = row_at(k), st = st + 1 == NST ? 0 : st + 1) {
     u32x4 b[CH][4];
     // issued after this row's loads: the loads of the next NST - 1 rows (those
     // that exist), and the stores of the rows processed since this row's
     // loads were issued (up to NST of them; a wave's last fp6 flush is never
-    // followed by a wait)
+    // followed by a wait).  The setup's sign loads, issued after the first
+    // NST rows' loads, are left out: a count below the true one only waits
+    // longer.
     int younger = 0;
 #pragma unroll
     for (int i = 1; i < NST; ++i)
@@ -481,11 +497,25 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
 
 template <int G, bool SCALE_F16, bool OUT_F32, int BITS = 4>
 static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
-  // 4 waves per block, one row per wave (fp6: a group of 4 rows per wave)
-  int64_t blocks = BITS == 6 ? (a.rows + 15) / 16 : (a.rows + 3) / 4;
-  const int64_t cap =
+  // 4 waves per block.  Units of work: rows, or for fp6 groups of 4 rows.
+  // Up to one grid of resident workgroups, a unit per wave.  Beyond that,
+  // UPW units per wave in at least two rounds of resident workgroups, so
+  // that the hardware hands the later ones to the CUs that finish first
+  // (bf16 65536 x 2048, HBM-resident, same box: 8 rows per wave 58.2-58.7
+  // us, 16 (one resident grid) 61.3 us, 4 58.6-59.0 us, 2 63.6 us); with
+  // fewer, one resident grid (a partial second round idles most of the chip:
+  // int8 20000 x 4096 took 56.7 us spread over 1.2 rounds, 51.1 us
+  // resident).  The fp32 output of 2048-point rows stays on one resident
+  // grid (145.1 against 149.7 us spread).
+  constexpr int64_t UPW = BITS == 6 ? 2 : 8;
+  const int64_t units = BITS == 6 ? (a.rows + 3) / 4 : a.rows;
+  const int64_t resident =
       256 * (a.p == 4096 ? mfma_blocks_per_cu<OUT_F32, 2, BITS>() : mfma_blocks_per_cu<OUT_F32, 1, BITS>());
-  if (blocks > cap) blocks = cap;
+  int64_t blocks = (units + 3) / 4;
+  if (blocks > resident) {
+    const int64_t spread = (units + 4 * UPW - 1) / (4 * UPW);
+    blocks = (spread < 2 * resident || (OUT_F32 && a.p == 2048)) ? resident : spread;
+  }
   if (a.p == 4096)
     hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS, 2>), dim3((unsigned)blocks),
                        dim3(256), 0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
