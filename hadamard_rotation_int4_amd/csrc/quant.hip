@@ -43,19 +43,20 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const void* __rest
     const bool live = o < octets;
     float y[8];
     if (IN_BF16) {
-      const uint4 r = live ? reinterpret_cast<const uint4*>(x)[o] : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+      // nontemporal loads: the input is read once
+      const u32x4 r = live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + o) : (u32x4){0u, 0u, 0u, 0u};
+      const uint32_t w[4] = {r[0], r[1], r[2], r[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         y[2 * i] = __uint_as_float(w[i] << 16);
         y[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
       }
     } else {
-      const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      const float4 r0 = live ? reinterpret_cast<const float4*>(x)[2 * o] : z;
-      const float4 r1 = live ? reinterpret_cast<const float4*>(x)[2 * o + 1] : z;
-      y[0] = r0.x; y[1] = r0.y; y[2] = r0.z; y[3] = r0.w;
-      y[4] = r1.x; y[5] = r1.y; y[6] = r1.z; y[7] = r1.w;
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      const f32x4 r0 = live ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + 2 * o) : z;
+      const f32x4 r1 = live ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + 2 * o + 1) : z;
+      y[0] = r0[0]; y[1] = r0[1]; y[2] = r0[2]; y[3] = r0[3];
+      y[4] = r1[0]; y[5] = r1[1]; y[6] = r1[2]; y[7] = r1[3];
     }
     float m = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fabsf(y[2]));
     m = fmaxf(fmaxf(m, fabsf(y[3])), fabsf(y[4]));
@@ -127,7 +128,11 @@ static void launch_q2(const QuantArgs& a, int64_t octets, int64_t blocks, hipStr
 hipError_t launch_quant(const QuantArgs& a, hipStream_t s) {
   const int64_t octets = a.rows * (int64_t)(a.n / 8);
   int64_t blocks = (octets + kQuantThreads - 1) / kQuantThreads;
-  if (blocks > 2048) blocks = 2048;   // eight workgroups per CU, grid-stride beyond
+  // one octet per lane: the hardware hands workgroups to the CUs that finish
+  // first (bf16 65536 x 2048, G = 128, HBM-resident, same box, with the
+  // nontemporal loads: 63.8 -> 57.4 us against a grid of 2048 workgroups
+  // striding over the rows); grid-stride only beyond 2^20 workgroups
+  if (blocks > (1 << 20)) blocks = 1 << 20;
   switch (a.group) {
     case 32: launch_q2<32>(a, octets, blocks, s); break;
     case 64: launch_q2<64>(a, octets, blocks, s); break;
