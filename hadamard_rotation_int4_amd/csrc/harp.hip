@@ -35,7 +35,7 @@ constexpr int kHarpThreads = 1024;
 // 16-byte global -> LDS copy (LDS-DMA: lane i's 16 bytes land at lp + 16 i)
 // nt: with the nontemporal hint.  Measured on fp32 4096 x 5120, two buffer
 // sets in turn, same box: with fp32 output 82.0 -> 75.5 us, with int4 codes
-// 85.9 -> 87.5 us, so only the fp32 output takes it.
+// 85.9 -> 87.5 us, so only the fp32 output of a streamed input takes it.
 __device__ __forceinline__ void harp_lds_load16(const void* gp, void* lp, bool nt) {
   if (nt) __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 2);
   else __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kHarpThreads) void harp_apply_kernel(HarpArgs a) {
       const int p = 64 * u + ln;
       if (p < npc) {
         const int r = p / q4, k = p - r * q4;
-        harp_lds_load16(src + r * q4 + (hswz(4 * k, swz) >> 2), lds + 256 * u, a.codes == nullptr);
+        harp_lds_load16(src + r * q4 + (hswz(4 * k, swz) >> 2), lds + 256 * u, a.stream != 0);
       }
     }
     // (each stage starts with the barrier that waits for these loads or the
@@ -257,6 +257,7 @@ hipError_t launch_harp_apply(HarpArgs a, hipStream_t s) {
   while (R > 1 && ((int64_t)R * a.d + 255) / 256 * 256 > 40960) --R;
   if (R < 1) R = 1;
   a.rows_per_group = R;
+  a.stream = a.codes == nullptr && a.rows * a.d * 4 >= kStreamBytes;
   const int64_t ngroups = (a.rows + R - 1) / R;
   const int64_t grid = ngroups < 512 ? ngroups : 512;
   const size_t lds = sizeof(float) * (((size_t)R * a.d + 255) / 256 * 256);

@@ -84,8 +84,27 @@ __device__ __forceinline__ int mfma2048_a4(int q) {
   return (q & 12) | ((q ^ (q >> 2)) & 1) | ((((q >> 1) ^ (q >> 2)) & 1) << 1);
 }
 
+// The sign bytes of a lane's B operands (8 per K-step), loaded apart from
+// the rest of the setup: a kernel can issue these loads ahead of its first
+// row loads and compute the setup after them.
+struct Mfma2048Signs {
+  uint2 s8[4];
+};
+
+// All +1: read in place of a null sign vector, so that the loads are
+// unconditional (a value merged from a load and a constant would make the
+// compiler wait for the load at the merge).
+static __device__ int8_t kMfmaNoSigns[2048] = {};
+
 // signs: the chunk's 2048 signs (int8 +-1) or null (all +1).
-__device__ __forceinline__ void mfma2048_init(Mfma2048& M, int lane, const int8_t* signs) {
+__device__ __forceinline__ void mfma2048_load_signs(Mfma2048Signs& S, int lane, const int8_t* signs) {
+  const int a4 = mfma2048_a4(lane & 15), g = lane >> 4;
+  const int8_t* sp = signs ? signs : kMfmaNoSigns;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) S.s8[s] = *reinterpret_cast<const uint2*>(sp + a4 * 128 + 32 * s + 8 * g);
+}
+
+__device__ __forceinline__ void mfma2048_init(Mfma2048& M, int lane, const Mfma2048Signs& S) {
   const int q = lane & 15, g = lane >> 4;
   const int a4 = mfma2048_a4(q);
   M.q = q;
@@ -113,16 +132,14 @@ __device__ __forceinline__ void mfma2048_init(Mfma2048& M, int lane, const int8_
     }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (signs) {
-      const uint2 s8 = *reinterpret_cast<const uint2*>(signs + a4 * 128 + 32 * s + 8 * g);
+    // (no signs: zero bytes, zero masks)
+    uint32_t w[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t src = d < 2 ? s8.x : s8.y;
-        const uint32_t b0 = (src >> (16 * (d & 1))) & 0x80u;
-        const uint32_t b1 = (src >> (16 * (d & 1) + 8)) & 0x80u;
-        w[d] = (b0 << 8) | (b1 << 24);
-      }
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t src = d < 2 ? S.s8[s].x : S.s8[s].y;
+      const uint32_t b0 = (src >> (16 * (d & 1))) & 0x80u;
+      const uint32_t b1 = (src >> (16 * (d & 1) + 8)) & 0x80u;
+      w[d] = (b0 << 8) | (b1 << 24);
     }
     M.sm[s] = (u32x4){w[0], w[1], w[2], w[3]};
   }
@@ -131,6 +148,12 @@ __device__ __forceinline__ void mfma2048_init(Mfma2048& M, int lane, const int8_
   M.beta2 = (a4 & 4) ? -1.0f : 1.0f;
   M.beta3 = (a4 & 8) ? -1.0f : 1.0f;
   M.tau = (__builtin_popcount(a4) & 1) ? -1.0f : 1.0f;
+}
+
+__device__ __forceinline__ void mfma2048_init(Mfma2048& M, int lane, const int8_t* signs) {
+  Mfma2048Signs S;
+  mfma2048_load_signs(S, lane, signs);
+  mfma2048_init(M, lane, S);
 }
 
 // Transform one chunk: b[s] are the lane's raw bf16 B operands; on return

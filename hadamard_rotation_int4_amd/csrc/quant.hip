@@ -27,7 +27,7 @@ template <int G, int BITS, bool SCALE_F16, bool IN_BF16>
 __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const void* __restrict__ x,
                                                               int64_t octets,
                                                               uint8_t* __restrict__ codes,
-                                                              void* __restrict__ scales) {
+                                                              void* __restrict__ scales, bool nt) {
   constexpr int L = G / 8;                       // lanes per group
   constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
   // y k + M leaves the rounded code in the low mantissa bits (ties to even);
@@ -43,8 +43,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const void* __rest
     const bool live = o < octets;
     float y[8];
     if (IN_BF16) {
-      // nontemporal loads: the input is read once
-      const u32x4 r = live ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + o) : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4* xp = reinterpret_cast<const u32x4*>(x) + o;
+      const u32x4 r = live ? (nt ? __builtin_nontemporal_load(xp) : *xp) : (u32x4){0u, 0u, 0u, 0u};
       const uint32_t w[4] = {r[0], r[1], r[2], r[3]};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -53,8 +53,9 @@ __global__ __launch_bounds__(kQuantThreads) void quant_kernel(const void* __rest
       }
     } else {
       const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const f32x4 r0 = live ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + 2 * o) : z;
-      const f32x4 r1 = live ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x) + 2 * o + 1) : z;
+      const f32x4* xp = reinterpret_cast<const f32x4*>(x) + 2 * o;
+      const f32x4 r0 = live ? (nt ? __builtin_nontemporal_load(xp) : xp[0]) : z;
+      const f32x4 r1 = live ? (nt ? __builtin_nontemporal_load(xp + 1) : xp[1]) : z;
       y[0] = r0[0]; y[1] = r0[1]; y[2] = r0[2]; y[3] = r0[3];
       y[4] = r1[0]; y[5] = r1[1]; y[6] = r1[2]; y[7] = r1[3];
     }
@@ -108,10 +109,12 @@ template <int G, int BITS, bool F16>
 static void launch_q3(const QuantArgs& a, int64_t octets, int64_t blocks, hipStream_t s) {
   if (a.x_bf16)
     hipLaunchKernelGGL((quant_kernel<G, BITS, F16, true>), dim3((unsigned)blocks), dim3(kQuantThreads),
-                       0, s, a.x, octets, a.codes, a.scales);
+                       0, s, a.x, octets, a.codes, a.scales,
+                       octets * (a.x_bf16 ? 16 : 32) >= kStreamBytes);
   else
     hipLaunchKernelGGL((quant_kernel<G, BITS, F16, false>), dim3((unsigned)blocks), dim3(kQuantThreads),
-                       0, s, a.x, octets, a.codes, a.scales);
+                       0, s, a.x, octets, a.codes, a.scales,
+                       octets * (a.x_bf16 ? 16 : 32) >= kStreamBytes);
 }
 
 template <int G>

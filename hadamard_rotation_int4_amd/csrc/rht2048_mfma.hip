@@ -59,19 +59,21 @@ constexpr int mfma_blocks_per_cu() {
   return BITS == 6 ? (CH == 2 ? 1 : 2) : (OUT_F32 && CH == 2) ? 1 : (OUT_F32 || CH == 2) ? 2 : 3;
 }
 
-// 16-byte global -> LDS copy, nontemporal (the builtin sits in a device
-// function: used directly in a kernel template it can cost the instance its
-// host stub).  With HBM-resident input (bf16 65536 x 2048, three buffer
-// sets, same box) the nontemporal hint on whole-line loads took the kernel
+// 16-byte global -> LDS copy, nontemporal when nt (the builtin sits in a
+// device function: used directly in a kernel template it can cost the
+// instance its host stub).  With HBM-resident input (bf16 65536 x 2048,
+// three buffer sets, same box) the hint on whole-line loads took the kernel
 // from 63.8 to 62.9 us; on the earlier 64-byte runs it had cost 0.7 us.
-__device__ __forceinline__ void mfma_lds_load16(const void* gp, void* lp) {
-  __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 2);
+__device__ __forceinline__ void mfma_lds_load16(const void* gp, void* lp, bool nt) {
+  if (nt) __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 2);
+  else __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
 }
 
 template <int G, bool SCALE_F16, bool OUT_F32, int BITS, int CH = 1>
 __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) void rht2048_mfma_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ signs, int64_t rows,
-    float* __restrict__ yout, uint8_t* __restrict__ codes, void* __restrict__ scales, float norm) {
+    float* __restrict__ yout, uint8_t* __restrict__ codes, void* __restrict__ scales, float norm,
+    bool nt) {
   static_assert(CH == 1 || CH == 2, "rows of one or two 2048-point chunks");
   constexpr int P = 2048;          // chunk
   constexpr int N = CH * P;        // row
@@ -88,8 +90,12 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
     if (BITS == 6) return 4 * (wave + (int64_t)(k >> 2) * nwaves) + (k & 3);
     return wave + (int64_t)k * nwaves;
   };
-  // (initialized after the first rows' loads are issued, so that the sign
-  // loads and the setup overlap them: 62.9 -> 60.6 us, same box)
+  // (the sign loads go first; the rest of the setup is computed after the
+  // first rows' loads are issued, so that it overlaps them: 62.9 -> 60.6 us,
+  // same box, bf16 65536 x 2048)
+  Mfma2048Signs SG[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) mfma2048_load_signs(SG[c], lane, signs ? signs + c * P : nullptr);
   Mfma2048 M[CH];
   const int g = lane >> 4, a4 = mfma2048_a4(lane & 15);
   const float tau = (__builtin_popcount(a4) & 1) ? -1.0f : 1.0f;
@@ -113,12 +119,19 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
     lane_src[j] = 512 * j + 128 * h + 8 * u;
   }
   auto issue = [&](int64_t row, int st) {
+    // (one branch on nt per row, not one per load)
+    if (nt) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint16_t* base = x + row * N + c * P;
+      for (int c = 0; c < CH; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        mfma_lds_load16(base + lane_src[j], &stage_lds[wib][st][256 * c + 64 * j]);
+        for (int j = 0; j < 4; ++j)
+          mfma_lds_load16(x + row * N + c * P + lane_src[j], &stage_lds[wib][st][256 * c + 64 * j], true);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          mfma_lds_load16(x + row * N + c * P + lane_src[j], &stage_lds[wib][st][256 * c + 64 * j], false);
     }
   };
   // B operands of one row from stage st: lane (q, g) takes piece 4 s + g of
@@ -472,15 +485,13 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
   for (int i = 0; i < NST; ++i)
     if (row_at(i) < rows) issue(row_at(i), i);
 #pragma unroll
-  for (int c = 0; c < CH; ++c) mfma2048_init(M[c], lane, signs ? signs + c * P : nullptr);
+  for (int c = 0; c < CH; ++c) mfma2048_init(M[c], lane, SG[c]);
   for (int st = 0, k = 0; row < rows; ++k, row = row_at(k), st = st + 1 == NST ? 0 : st + 1) {
     u32x4 b[CH][4];
     // issued after this row's loads: the loads of the next NST - 1 rows (those
     // that exist), and the stores of the rows processed since this row's
     // loads were issued (up to NST of them; a wave's last fp6 flush is never
-    // followed by a wait).  The setup's sign loads, issued after the first
-    // NST rows' loads, are left out: a count below the true one only waits
-    // longer.
+    // followed by a wait).
     int younger = 0;
 #pragma unroll
     for (int i = 1; i < NST; ++i)
@@ -516,14 +527,15 @@ static void launch_mfma(const RhtArgs& a, float norm, hipStream_t s) {
     const int64_t spread = (units + 4 * UPW - 1) / (4 * UPW);
     blocks = (spread < 2 * resident || (OUT_F32 && a.p == 2048)) ? resident : spread;
   }
+  const bool nt = a.rows * a.n * 2 >= kStreamBytes;
   if (a.p == 4096)
     hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS, 2>), dim3((unsigned)blocks),
                        dim3(256), 0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
-                       a.scales, norm);
+                       a.scales, norm, nt);
   else
     hipLaunchKernelGGL((rht2048_mfma_kernel<G, SCALE_F16, OUT_F32, BITS>), dim3((unsigned)blocks),
                        dim3(256), 0, s, static_cast<const uint16_t*>(a.x), a.signs, a.rows, a.y, a.codes,
-                       a.scales, norm);
+                       a.scales, norm, nt);
 }
 
 // bf16 rows of n = 2048 or 4096: fused int4 quantization with the codes in
