@@ -240,6 +240,12 @@ def main(argv=None):
     ap.add_argument("--profile-mixed", action="store_true",
                     help="run only the bf16 16384x14336 (m = 7) mixed-radix quantization, --steps times "
                          "(for counters)")
+    ap.add_argument("--profile-butterfly", action="store_true",
+                    help="run only the fp32 32768x4096 butterfly, fp32 output and G=64 codes only, --steps "
+                         "times each (for counters)")
+    ap.add_argument("--profile-harp", action="store_true",
+                    help="run only the HARP processor on fp32 4096x5120, (8, 8, 8, 5, 2), fp32 output, "
+                         "--steps times (for counters)")
     ap.add_argument("--profile-run", action="store_true",
                     help="run the headline kernel and a plain copy (for rocprofv3 --pmc), print nothing")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -296,6 +302,30 @@ def main(argv=None):
         sm = torch.empty((mi.rows, mi.m * mi.p // 128), dtype=torch.float16, device=dev)
         for _ in range(args.steps):
             hr.rotate_quant_int4(xm, 128, dm, om, codes=cm, scales=sm)
+        torch.cuda.synchronize()
+        return 0
+
+    if args.profile_butterfly:
+        bi = hr_inputs.butterfly_inputs()
+        xb = torch.from_numpy(bi.x).to(dev)
+        co = hr.butterfly_coeffs(torch.from_numpy(bi.angles).to(dev), False)
+        pb = torch.from_numpy(bi.perm).to(dev)
+        yb = torch.empty_like(xb)
+        for _ in range(args.steps):
+            hr.butterfly_apply(xb, co, False, pb, out=yb)
+        for _ in range(args.steps):
+            hr.butterfly_apply(xb, co, False, pb, want_y=False, group=64)
+        torch.cuda.synchronize()
+        return 0
+
+    if args.profile_harp:
+        hi = hr_inputs.harp_inputs()
+        fb = torch.from_numpy(np.concatenate([f.ravel() for f in hi.fallbacks])).to(dev)
+        hblk = hr.harp_blocks(hi.radices, torch.from_numpy(hi.theta).to(dev), fb)
+        hx = [torch.from_numpy(hi.x).to(dev) for _ in range(2)]
+        hy = [torch.empty_like(hx[0]) for _ in range(2)]
+        for i in range(args.steps):
+            hr.harp_apply(hx[i % 2], hi.radices, hblk, out=hy[i % 2])
         torch.cuda.synchronize()
         return 0
 
@@ -680,11 +710,34 @@ def _summarize_mixed_counters(d):
                         "--profile-mixed")
 
 
+def _summarize_butterfly_counters(d):
+    _summarize_counters(d, "bf_p", (("fp32 output", "butterfly4096_kernel<false, false, true, 0, false>"),
+                                    ("codes only, G = 64", "butterfly4096_kernel<false, false, false, 64, true>")),
+                        "butterfly4096_32768x4096.counters.txt",
+                        "the fp32 32768x4096 butterfly (12 Givens stages + gather), fp32 output and G=64 codes only",
+                        "--profile-butterfly")
+
+
+def _summarize_harp_counters(d):
+    _summarize_counters(d, "harp_p", (("HARP apply, fp32 output", "harp_apply_kernel"),),
+                        "harp_apply_f32_4096x5120_r88852.counters.txt",
+                        "the HARP processor on fp32 4096x5120, schedule (8, 8, 8, 5, 2), fp32 output",
+                        "--profile-harp")
+
+
 def summarize_profile(d):
     """Write the kernel-duration summary and the HBM-traffic summary of the
     headline kernel from rocprofv3 outputs under d/ktrace, d/fetch, d/write."""
     os.makedirs(PROFILES, exist_ok=True)
+    # each summary is written only from runs present under d (the counter
+    # passes of one kernel can be refreshed without the others)
+    _summarize_gemm_counters(d)
+    _summarize_mixed_counters(d)
+    _summarize_butterfly_counters(d)
+    _summarize_harp_counters(d)
     stats = _read_csv(os.path.join(d, "ktrace", "**", "*kernel_stats.csv"))
+    if not stats:
+        return 0
     lines = ["# rocprofv3 --kernel-trace --stats summary (times in microseconds)",
              "# command: rocprofv3 --kernel-trace --stats -d <dir>/ktrace -o run --output-format csv -- "
              "python3 bench.py --no-cpu-baseline",
@@ -715,8 +768,8 @@ def summarize_profile(d):
            "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw, "dispatches": nk,
            "copy_kernel_match": copy_kernel, "copy_bytes": COPY_BYTES, "copy_fetch_kib": cf,
            "copy_write_kib": cw, "copy_dispatches": nc}
-    _summarize_gemm_counters(d)
-    _summarize_mixed_counters(d)
+    if nk == 0:
+        return 0
     if None not in (kf, kw, cf, cw):
         ff = COPY_BYTES / (cf * 1024.0)
         fw = COPY_BYTES / (cw * 1024.0)

@@ -42,11 +42,17 @@ __device__ __forceinline__ void harp_lds_load16(const void* gp, void* lp, bool n
 }
 
 // LDS position of in-row element i when 64 divides d: bits 2-5 XORed with
-// bits 6-9 of i, a permutation inside every aligned block of 64 elements.
-// The stride-S gathers of the 5120 schedule then put at most 4, 2, 1, 1, 1
-// lanes on a bank (stages 0 .. 4), against 8, 8, 1, 1, 1 unswizzled; groups
-// of 4 stay contiguous, so rows still move as float4.
-__device__ __forceinline__ int hswz(int i, bool on) { return on ? i ^ (((i >> 6) & 15) << 2) : i; }
+// h(x) = x ^ ((x & 1) << 3) of x = bits 6-9 of i, a permutation inside every
+// aligned block of 64 elements and its own inverse.  Groups of 4 stay
+// contiguous, so rows move as float4.  For the 5120 schedule, the stride-S
+// element accesses of stages 1 .. 4 then reach 64 different banks per wave
+// (plain bits 6-9 left 2 lanes per bank in stage 1; unswizzled, 8), and
+// stage 0 (S = 1), whose blocks are contiguous, moves 16-byte pieces that
+// reach 16 different 16-byte bank groups per 16 lanes.
+__device__ __forceinline__ int hswz(int i, bool on) {
+  const int x = (i >> 6) & 15;
+  return on ? i ^ ((x ^ ((x & 1) << 3)) << 2) : i;
+}
 struct HarpPos {
   bool on;
   __device__ int operator()(int i) const { return hswz(i, on); }
@@ -147,6 +153,35 @@ __device__ __forceinline__ void harp_block(const float (&m)[B][B], float* lds, i
                                            bool swz) {
   const int lo = c % S, hi = c / S;
   const int base = lo + S * B * hi;
+  if constexpr (B % 4 == 0) {
+    if (S == 1 && (d & 3) == 0) {
+      // contiguous block: B / 4 float4 pieces (whole under the swizzle)
+      int p4[B / 4];
+#pragma unroll
+      for (int j = 0; j < B / 4; ++j) p4[j] = hswz(base + 4 * j, swz);
+      for (int r = 0; r < R; ++r) {
+        float* row = lds + r * d;
+        float v[B];
+#pragma unroll
+        for (int j = 0; j < B / 4; ++j) {
+          const float4 x = *reinterpret_cast<const float4*>(row + p4[j]);
+          v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+        }
+        float o[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int q = 0; q < B; ++q) acc = fmaf(m[i][q], v[q], acc);
+          o[i] = acc;
+        }
+#pragma unroll
+        for (int j = 0; j < B / 4; ++j)
+          *reinterpret_cast<float4*>(row + p4[j]) = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+      }
+      return;
+    }
+  }
   int pos[B];
 #pragma unroll
   for (int q = 0; q < B; ++q) pos[q] = hswz(base + q * S, swz);
