@@ -217,6 +217,26 @@ def test_mixed_radix_many_rows(m, group, with_signs, scale_mode):
     check_quant(codes.cpu().numpy(), scales.cpu().numpy(), y64, group, scale_mode)
 
 
+@pytest.mark.parametrize("m,scale_mode", [(2, "f16"), (3, "f32"), (7, "f16"), (7, "f32")])
+def test_mixed_radix_rows_per_wave(m, scale_mode):
+    """G = 128 codes with a dense block over 2125 rows: every workgroup of the
+    persistent grid takes four or five rows in turn, and the last round is
+    partial.  Sampled rows from every round against the oracle."""
+    hr = _hr()
+    rows, p = 2125, 2048
+    mi = hr_inputs.mixed_inputs(rows=rows, m=m, p=p, seed=360 + m)
+    xd = mi.x.to(DEV)
+    dd = torch.from_numpy(mi.signs).to(DEV)
+    od = torch.from_numpy(mi.block).to(DEV)
+    sd = torch.float16 if scale_mode == "f16" else torch.float32
+    codes, scales = hr.rotate_quant_int4(xd, 128, dd, od, scale_dtype=sd)
+    rng = np.random.default_rng(m)
+    sample = np.unique(np.concatenate([rng.choice(rows, 24, replace=False),
+                                       [0, 1, 1023, 1024, 1025, 2047, 2048, 2049, rows - 1]]))
+    y64 = oracle.mixed_radix.mixed_radix(mi.x[sample].float().numpy(), mi.signs, mi.block, p)
+    check_quant(codes.cpu().numpy()[sample], scales.cpu().numpy()[sample], y64, 128, scale_mode)
+
+
 @pytest.mark.parametrize("group", [32, 64, 128, 256])
 @pytest.mark.parametrize("m", [2, 3, 4, 5, 6, 7, 8])
 def test_mixed_radix_grid(m, group):
