@@ -29,6 +29,17 @@ namespace hr {
 constexpr int kMixWaves = 8;
 constexpr int kMixBlocksPerCu = 2;
 
+// Lane r's value of each quad, to the whole quad (DPP quad_perm [r, r, r, r];
+// r a constant once the caller's loop is unrolled).
+__device__ __forceinline__ float quad_bcast(float v, int r) {
+  switch (r) {
+    case 0: return dpp<0x00>(v);
+    case 1: return dpp<0x55>(v);
+    case 2: return dpp<0xAA>(v);
+    default: return dpp<0xFF>(v);
+  }
+}
+
 // LDS slot of 16-byte slot j (0..31) of 128-element block a (0..15).  A
 // 16-byte access is served 8 lanes at a time, so every aligned group of 8
 // lanes must reach 8 different 16-byte bank groups (mod 8), and 16 lanes 16
@@ -228,29 +239,39 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
 #pragma unroll
         for (int r = 0; r < OA; ++r) am[r] = umax_row_pair(am[r]);
       }
+      // the scale arithmetic once per lane: lane r of each quad (a quad lies
+      // inside one group, G / 8 >= 4 lanes) takes output r, and DPP quad
+      // broadcasts hand every lane the multipliers of all outputs
+      const int rl = lane & 3;
+      uint32_t amsel = am[0];
+#pragma unroll
+      for (int r = 1; r < OA; ++r) amsel = rl == r ? am[r] : amsel;
+      const bool rvalid = rl < nout;
+      const float s32 = div_const<7>(__uint_as_float(amsel) * norm);
+      const float sq = SF16 ? (float)(_Float16)s32 : s32;
+      // an fp32 scale below 2^-100 would overflow its reciprocal: the group's
+      // values and scale are then both taken x 2^64 (exact)
+      const float up = (!SF16 && sq < 0x1p-100f) ? 0x1p64f : 1.0f;
+      const float kq = sq > 0.0f ? norm * taug * __builtin_amdgcn_rcpf(sq * up) : 0.0f;
+      // the clamp and the x 2^64 only where some group of the wave needs
+      // them (a wave-uniform branch)
+      const bool clamp = __builtin_amdgcn_ballot_w64(
+                             rvalid && sq > 0.0f && sq < (SF16 ? 6.103515625e-05f : 1.17549435e-38f)) != 0;
+      const bool tiny = !SF16 && __builtin_amdgcn_ballot_w64(rvalid && sq > 0.0f && sq < 0x1p-100f) != 0;
+      // the group's first quad stores the scales: lane r that of output r
+      if ((lane & (G / 8 - 1)) < 4 && rvalid) {
+        const int so = ((ob + rl) * (P / G) + pos / G) * (SF16 ? 2 : 4);
+        if (SF16)
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)s32), rsc, so, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32), rsc, so, 0, 0);
+      }
 #pragma unroll
       for (int r = 0; r < OA; ++r) {
         if (r >= nout) break;
         const int bo = ob + r;
-        const float s32 = div_const<7>(__uint_as_float(am[r]) * norm);
-        const float sq = SF16 ? (float)(_Float16)s32 : s32;
-        // an fp32 scale below 2^-100 would overflow its reciprocal: the
-        // group's values and scale are then both taken x 2^64 (exact)
-        const float up = (!SF16 && sq < 0x1p-100f) ? 0x1p64f : 1.0f;
-        const float kq = sq > 0.0f ? norm * taug * __builtin_amdgcn_rcpf(sq * up) : 0.0f;
-        // the clamp and the x 2^64 only where some group of the wave needs
-        // them (a wave-uniform branch)
-        const bool clamp = __builtin_amdgcn_ballot_w64(
-                               sq > 0.0f && sq < (SF16 ? 6.103515625e-05f : 1.17549435e-38f)) != 0;
-        const bool tiny = !SF16 && __builtin_amdgcn_ballot_w64(sq > 0.0f && sq < 0x1p-100f) != 0;
-        // the first lane of each group stores its scale
-        if ((lane & (G / 8 - 1)) == 0) {
-          const int so = (bo * (P / G) + pos / G) * (SF16 ? 2 : 4);
-          if (SF16)
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)s32), rsc, so, 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s32), rsc, so, 0, 0);
-        }
+        const float kr = quad_bcast(kq, r);
+        const float ur = SF16 ? 1.0f : quad_bcast(up, r);
         // q + 1.5 * 2^23 + 8 rounds y k to an integer in the low mantissa
         // bits (ties to even); its low byte is q + 8 in [1, 15].  The clamp
         // to [-7, 7] only acts for fp16-subnormal (or fp32-denormal) scales,
@@ -258,7 +279,7 @@ __global__ __launch_bounds__(kMixWaves * 64, kMixBlocksPerCu) void mixed2048_mfm
         constexpr float MQ = 12582920.0f;
         float qf[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[e] = fmaf(tiny ? acc[e][r] * up : acc[e][r], kq, MQ);
+        for (int e = 0; e < 8; ++e) qf[e] = fmaf(tiny ? acc[e][r] * ur : acc[e][r], kr, MQ);
         if (clamp) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) qf[e] = __builtin_amdgcn_fmed3f(qf[e], MQ - 7.0f, MQ + 7.0f);
