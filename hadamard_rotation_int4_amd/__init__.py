@@ -21,7 +21,7 @@ import torch
 from . import srchash
 
 __all__ = ["HRError", "rotate", "rotate_quant_int4", "rotate_quant_int8", "quant_int4", "quant_int8",
-           "butterfly_coeffs", "butterfly_apply", "harp_blocks", "harp_apply", "harp_n_params",
+           "butterfly_coeffs", "butterfly_apply", "harp_blocks", "harp_apply", "harp_n_params", "harp_table_size",
            "dequant_int4", "w4a4_gemm", "w4a8_gemm", "w8a8_gemm", "rotate_quant_w4a4_gemm",
            "fp6_rows", "w4a4_to_fp6", "rotate_quant_fp6", "w4a4_gemm_fp6",
            "lib", "LIB_PATH", "SYMBOLS",
@@ -349,6 +349,16 @@ def _radices(radices):
     return r, len(rs), rs, d
 
 
+def harp_table_size(radices) -> int:
+    """Floats in the block table of a schedule: per stage ceil(b^2 / 4) quads
+    of d / b blocks."""
+    rs = [int(b) for b in radices]
+    d = 1
+    for b in rs:
+        d *= b
+    return sum(4 * ((b * b + 3) // 4) * (d // b) for b in rs)
+
+
 def harp_blocks(radices, theta: torch.Tensor, fallbacks: torch.Tensor | None = None) -> torch.Tensor:
     """Dense blocks of a HARP schedule (hr_harp_blocks).  radices: a Python
     sequence; theta: fp32 parameters [sum_t (d/b_t) P_t]; fallbacks: fp32
@@ -359,7 +369,7 @@ def harp_blocks(radices, theta: torch.Tensor, fallbacks: torch.Tensor | None = N
     n_fb = sum(b * b for b in rs if b & (b - 1))
     at = _arg(theta, "theta", torch.float32, (n_theta,))
     af = _arg(fallbacks, "fallbacks", torch.float32, (n_fb,))
-    blocks = torch.empty(d * sum(rs), dtype=torch.float32, device=theta.device)
+    blocks = torch.empty(harp_table_size(rs), dtype=torch.float32, device=theta.device)
     pt, pf, pb = _ptrs(at, af, ("blocks", blocks))
     _check(lib.hr_harp_blocks(arr, m, pt, pf, pb, _stream(theta.device)), "hr_harp_blocks")
     return blocks
@@ -375,7 +385,7 @@ def harp_apply(x: torch.Tensor, radices, blocks: torch.Tensor, inverse: bool = F
     if dd != d:
         raise ValueError(f"the radices multiply to {dd}, but rows have {d} elements")
     ax = _arg(x, "x", torch.float32, (rows, d))
-    ab = _arg(blocks, "blocks", torch.float32, (d * sum(rs),))
+    ab = _arg(blocks, "blocks", torch.float32, (harp_table_size(rs),))
     _arg(out, "out", torch.float32, (rows, d))
     g, sd, sdt = 0, HR_F16, None
     if group is not None:

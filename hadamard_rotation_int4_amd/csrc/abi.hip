@@ -284,7 +284,7 @@ static int32_t harp_schedule(const char* fn, const int32_t* radices, int32_t nst
     nblk += d / b;
     th += (d / b) * (b == 2 ? 1 : b * (b - 1) / 2);
     if (!pow2(b)) fb += (int64_t)b * b;
-    bo += d * b;
+    bo += (int64_t)4 * ((b * b + 3) / 4) * (d / b);   // quads of coefficients, the last one padded
   }
   sc->block_begin[nstages] = nblk;
   *d_out = (int32_t)d;

@@ -12,9 +12,13 @@
 //
 // harp_blocks_kernel: one thread per block, in double precision: Q (Givens,
 // or Gauss-Jordan solve of (I - A) Q = I + A), times G, stored as fp32.  The
-// table is coefficient-major per stage, [b][b][d/b]: coefficient (r, q) of
-// block c at (r b + q) d/b + c, so the lanes of a wave, which own consecutive
-// blocks, read each coefficient as one contiguous 256-byte run.
+// table is quad-major per stage, [ceil(b^2 / 4)][d/b][4]: coefficient k =
+// r b + q of block c at ((k / 4) d/b + c) 4 + k % 4 (the last quad padded with
+// zeros), so a thread loads its block's coefficients four at a time and the
+// lanes of a wave, which own consecutive blocks, read each quad as one
+// contiguous 1 KB run (four times fewer load instructions than one
+// coefficient per load: fp32 4096 x 5120, same box, 70.6 against 55.2 us
+// with no coefficient loads at all).
 // harp_apply_kernel: a persistent workgroup keeps R rows in LDS (loaded by
 // LDS-DMA, every load in flight at once) and runs every stage over them; each
 // thread takes blocks c = tid, tid + 1024, ..., holds the block's b^2
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(256) void harp_blocks_kernel(HarpSchedule sc, const
   const float* fb = fallbacks + sc.fallback_off[t];
   const double nrm = 1.0 / sqrt((double)b);
   const int64_t nb = sc.block_begin[t + 1] - sc.block_begin[t];
-  float* out = blocks + sc.blocks_off[t] + c;
+  float* out = blocks + sc.blocks_off[t] + 4 * c;
   for (int i = 0; i < b; ++i)
     for (int j = 0; j < b; ++j) {
       double s = 0.0;
@@ -125,26 +129,32 @@ __global__ __launch_bounds__(256) void harp_blocks_kernel(HarpSchedule sc, const
                                     : (double)fb[l * b + j];
         s += q[i][l] * g;
       }
-      out[(int64_t)(i * b + j) * nb] = (float)s;
+      const int k = i * b + j;
+      out[(int64_t)(k >> 2) * nb * 4 + (k & 3)] = (float)s;
     }
+  for (int k = b * b; k < 4 * ((b * b + 3) / 4); ++k) out[(int64_t)(k >> 2) * nb * 4 + (k & 3)] = 0.0f;
 }
 
-// The b^2 coefficients of block c (transposed for the inverse).
+// The b^2 coefficients of block c (transposed for the inverse), loaded four
+// at a time from the quad-major table.
 template <int B>
 __device__ __forceinline__ void harp_coeffs(float (&m)[B][B], const float* __restrict__ blk, int c, int nb,
                                             bool inverse) {
-  const float* src = blk + c;
-  if (inverse) {
+  constexpr int K4 = (B * B + 3) / 4;
+  const float4* src = reinterpret_cast<const float4*>(blk) + c;
+  float v[4 * K4];
 #pragma unroll
-    for (int i = 0; i < B; ++i)
-#pragma unroll
-      for (int j = 0; j < B; ++j) m[i][j] = src[(int64_t)(j * B + i) * nb];
-  } else {
-#pragma unroll
-    for (int i = 0; i < B; ++i)
-#pragma unroll
-      for (int j = 0; j < B; ++j) m[i][j] = src[(int64_t)(i * B + j) * nb];
+  for (int k = 0; k < K4; ++k) {
+    const float4 f = src[(int64_t)k * nb];
+    v[4 * k] = f.x;
+    v[4 * k + 1] = f.y;
+    v[4 * k + 2] = f.z;
+    v[4 * k + 3] = f.w;
   }
+#pragma unroll
+  for (int i = 0; i < B; ++i)
+#pragma unroll
+    for (int j = 0; j < B; ++j) m[i][j] = inverse ? v[j * B + i] : v[i * B + j];
 }
 
 // Map block c of one stage over the R rows in LDS.

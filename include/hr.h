@@ -258,9 +258,10 @@ int32_t hr_butterfly_apply(const float* x, float* y, int64_t rows, int32_t n,
  *   fallbacks  [b][b] fp32 orthogonal matrices (row-major), one per stage whose
  *              radix is not a power of two, concatenated in stage order; may be
  *              NULL when every radix is a power of two.  Used as given.
- *   blocks     output [sum_t d * b_t] fp32, stages concatenated in order; stage t
- *              is coefficient-major, [b_t][b_t][d/b_t]: entry (r, q) of block c
- *              at (r * b_t + q) * (d / b_t) + c.
+ *   blocks     output [sum_t 4 K_t (d / b_t)] fp32, K_t = ceil(b_t^2 / 4), stages
+ *              concatenated in order; stage t is quad-major, [K_t][d/b_t][4]:
+ *              entry k = r * b_t + q of block c at ((k / 4) * (d / b_t) + c) * 4
+ *              + k % 4; the K_t * 4 - b_t^2 padding entries of each block are 0.
  */
 int32_t hr_harp_blocks(const int32_t* radices, int32_t nstages, const float* theta,
                        const float* fallbacks, float* blocks, void* stream);

@@ -30,13 +30,18 @@ def _gpu_blocks(hi):
 
 
 def _split(flat, radices):
-    """The library's coefficient-major table ([b][b][d/b] per stage) as the
-    oracle's per-block list ([d/b][b][b] per stage)."""
+    """The library's quad-major table ([ceil(b^2/4)][d/b][4] per stage, the
+    last quad zero-padded) as the oracle's per-block list ([d/b][b][b] per
+    stage); the padding is checked to be zero."""
     d = int(np.prod(radices))
+    assert flat.size == _hr().harp_table_size(radices)
     out, off = [], 0
     for b in radices:
-        out.append(flat[off:off + d * b].reshape(b, b, d // b).transpose(2, 0, 1))
-        off += d * b
+        k4 = (b * b + 3) // 4
+        stage = flat[off:off + 4 * k4 * (d // b)].reshape(k4, d // b, 4).transpose(1, 0, 2).reshape(d // b, 4 * k4)
+        assert not stage[:, b * b:].any()
+        out.append(stage[:, :b * b].reshape(d // b, b, b))
+        off += 4 * k4 * (d // b)
     return out
 
 
