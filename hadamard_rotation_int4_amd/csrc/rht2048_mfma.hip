@@ -423,7 +423,7 @@ __global__ __launch_bounds__(256, (mfma_blocks_per_cu<OUT_F32, CH, BITS>())) voi
   auto flush6 = [&](int64_t r0) {
     const int64_t valid = rows - r0;
     const int64_t prow = (rows + 127) / 128 * 128;
-    if (lane < N / G) {
+    if (lane < N / (G ? G : 1)) {   // (G = 0, the fp32 output, never flushes)
       const uint8_t* src = &scale_lds[wib][4 * SES * lane];
       uint8_t* dst = static_cast<uint8_t*>(scales) + (lane * prow + r0) * SES;
       if (valid >= 4) {
