@@ -45,17 +45,29 @@ __device__ __forceinline__ void harp_lds_load16(const void* gp, void* lp, bool n
   else __builtin_amdgcn_global_load_lds(gp, (__attribute__((address_space(3))) void*)lp, 16, 0, 0);
 }
 
-// LDS position of in-row element i when 64 divides d: bits 2-5 XORed with
-// h(x) = x ^ ((x & 1) << 3) of x = bits 6-9 of i, a permutation inside every
-// aligned block of 64 elements and its own inverse.  Groups of 4 stay
-// contiguous, so rows move as float4.  For the 5120 schedule, the stride-S
-// element accesses of stages 1 .. 4 then reach 64 different banks per wave
-// (plain bits 6-9 left 2 lanes per bank in stage 1; unswizzled, 8), and
-// stage 0 (S = 1), whose blocks are contiguous, moves 16-byte pieces that
-// reach 16 different 16-byte bank groups per 16 lanes.
+// LDS position of in-row element i when 64 divides d: with x = bits 6-9 of
+// i, bits 2-5 XORed with t(x) = (x & 1) | ((x & 7) << 1), then bit 5 of the
+// result XORed into bit 2.  Both steps permute each aligned block of 64
+// elements, keep groups of 4 whole (rows move as float4) and are their own
+// inverses, so the inverse applies them in reverse order.  A 4-byte access is
+// served 32 lanes at a time over 32 banks, a 16-byte one 8 lanes at a time
+// over 8 16-byte bank groups.  For the schedules of radix-8 stages (5120 =
+// (8, 8, 8, 5, 2), 4096, 16384, ...) every stage's stride-S element accesses
+// then reach 32 different banks per half-wave and 64 per wave, and every
+// 16-byte access (the contiguous blocks of a stride-1 stage, the output copy,
+// the quantizer's reads) 8 different groups per 8 lanes and 16 per 16.  (The
+// first swizzle, bits 2-5 XORed with x ^ ((x & 1) << 3) alone, left 2 lanes
+// to a bank in every half-wave of the stride-8 stage and 2 lanes to a group
+// in the 16-byte reads of pieces 2i.)
 __device__ __forceinline__ int hswz(int i, bool on) {
   const int x = (i >> 6) & 15;
-  return on ? i ^ ((x ^ ((x & 1) << 3)) << 2) : i;
+  const int j = i ^ (((x & 1) | ((x & 7) << 1)) << 2);
+  return on ? j ^ ((j >> 3) & 4) : i;
+}
+__device__ __forceinline__ int hswz_inv(int k, bool on) {
+  const int j = k ^ ((k >> 3) & 4);
+  const int x = (j >> 6) & 15;
+  return on ? j ^ (((x & 1) | ((x & 7) << 1)) << 2) : k;
 }
 struct HarpPos {
   bool on;
@@ -239,8 +251,8 @@ __global__ __launch_bounds__(kHarpThreads) void harp_apply_kernel(HarpArgs a) {
     const int nr = (int)(a.rows - r0 < R ? a.rows - r0 : R);
     // load nr rows (float4; d is a multiple of 4) by LDS-DMA, 1 KB of LDS
     // per instruction and no registers held: LDS float4 p (row r, in-row k)
-    // takes the row's float4 whose swizzled place is k (the swizzle is its
-    // own inverse); every load is in flight before the barrier's wait
+    // takes the row's float4 whose swizzled place is k; every load is in
+    // flight before the barrier's wait
     const int q4 = d / 4, npc = nr * q4;
     const int wv = tid >> 6, ln = tid & 63;
     const float4* src = reinterpret_cast<const float4*>(a.x + r0 * d);
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(kHarpThreads) void harp_apply_kernel(HarpArgs a) {
       const int p = 64 * u + ln;
       if (p < npc) {
         const int r = p / q4, k = p - r * q4;
-        harp_lds_load16(src + r * q4 + (hswz(4 * k, swz) >> 2), lds + 256 * u, a.stream != 0);
+        harp_lds_load16(src + r * q4 + (hswz_inv(4 * k, swz) >> 2), lds + 256 * u, a.stream != 0);
       }
     }
     // (each stage starts with the barrier that waits for these loads or the
